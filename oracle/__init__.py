@@ -1,0 +1,155 @@
+"""CPU oracle for streaming sparse attention: test infrastructure only.
+
+This package wraps ``ssa_oracle.c`` (plain C, double precision) with ctypes.
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import it; the product library never does, and the two share no code.
+
+What the oracle computes, and the readings it takes where the pages are
+silent, is stated at the top of ``ssa_oracle.c``. In short (LongCat ZigZag
+Attention digest, section 01 part (1), the SSA paragraph, and part (2), the
+deployed configuration b=128, s=1, l=7): query i attends to key j iff
+``j <= i`` and ``j // b < s or j // b > i // b - l``, with scaled-dot-product
+softmax over those keys.
+
+Arrays are numpy: float32, or uint16 holding bfloat16 bit patterns (both are
+exact in double). Any strides are accepted as long as the last (head-dim)
+axis is contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssa_oracle.c")
+_LIB = os.path.join(_HERE, "libssa_oracle.so")
+_lib = None
+
+ELEM_F32 = 0
+ELEM_BF16 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no hand vectorisation)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        p, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_ssa_prefill.restype = i32
+        lib.oracle_ssa_prefill.argtypes = [i32, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                           i32, i32, i32, i32, dbl, p, i64, p, p, p]
+        lib.oracle_decode_paged.restype = i32
+        lib.oracle_decode_paged.argtypes = [i32, p, p, p, p, p, i64, p, i64, p, i32, i32, i32,
+                                            i32, i32, i32, i32, i32, i32, i32, dbl, p, p]
+        lib.oracle_max_threads.restype = i32
+        lib.oracle_set_threads.argtypes = [i32]
+        _lib = lib
+    return _lib
+
+
+def _elem(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return ELEM_F32
+    if a.dtype == np.uint16:
+        return ELEM_BF16
+    raise TypeError(f"oracle takes float32 or bfloat16 bits (uint16), got {a.dtype}")
+
+
+def _strides(a: np.ndarray, axes: int) -> np.ndarray:
+    if a.strides[-1] != a.itemsize:
+        raise ValueError("last axis must be contiguous")
+    return np.array([s // a.itemsize for s in a.strides[:axes]], dtype=np.int64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def prefill(q, k, v, *, block=128, sink=1, local=7, scale, full=False, rows=None,
+            weights=False):
+    """Attention of every (or every listed) query row of [B, N, H, d] inputs.
+
+    Returns ``(o, lse, w)``: o [B, R, Hq, d_v] float64, lse [B, Hq, R] float64,
+    w [B, Hq, R, N] float64 dense weights (only when ``weights``; else None).
+    ``full=True`` gives plain causal attention (the pattern is ignored).
+    """
+    lib = _load()
+    elem = _elem(q)
+    if _elem(k) != elem or _elem(v) != elem:
+        raise TypeError("q, k, v must share one element type")
+    B, N, Hq, d_qk = q.shape
+    Bk, Nk, Hkv, d_qk2 = k.shape
+    Bv, Nv, Hkv2, d_v = v.shape
+    if (Bk, Nk, d_qk2) != (B, N, d_qk) or (Bv, Nv, Hkv2) != (B, N, Hkv):
+        raise ValueError("shape mismatch")
+    rows_arr = None
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    R = N if rows_arr is None else rows_arr.size
+    o = np.empty((B, R, Hq, d_v), dtype=np.float64)
+    lse = np.empty((B, Hq, R), dtype=np.float64)
+    w = np.empty((B, Hq, R, N), dtype=np.float64) if weights else None
+    qs, ks, vs = _strides(q, 3), _strides(k, 3), _strides(v, 3)
+    rc = lib.oracle_ssa_prefill(elem, _ptr(q), _ptr(k), _ptr(v), _ptr(qs), _ptr(ks), _ptr(vs),
+                                B, N, Hq, Hkv, d_qk, d_v, block, sink, local, int(full),
+                                float(scale), _ptr(rows_arr), R, _ptr(o), _ptr(lse), _ptr(w))
+    if rc != 0:
+        raise ValueError("oracle_ssa_prefill rejected its arguments")
+    return o, lse, w
+
+
+def decode_paged(q, k_cache, v_cache, page_table, ctx_lens, *, block=128, sink=1, local=7,
+                 scale, full=False):
+    """One new query per sequence against a paged cache.
+
+    q [B, Hq, d_qk]; k_cache [pages, page_size, Hkv, d_qk]; v_cache
+    [pages, page_size, Hkv, d_v] (may be a view of k_cache); page_table
+    [B, max_pages] int32; ctx_lens [B] int32. Returns ``(o, lse)`` in float64.
+    """
+    lib = _load()
+    elem = _elem(q)
+    if _elem(k_cache) != elem or _elem(v_cache) != elem:
+        raise TypeError("q and caches must share one element type")
+    q = np.ascontiguousarray(q)
+    B, Hq, d_qk = q.shape
+    num_pages, page_size, Hkv, d_qk2 = k_cache.shape
+    num_pages2, page_size2, Hkv2, d_v = v_cache.shape
+    if d_qk2 != d_qk or (num_pages2, page_size2, Hkv2) != (num_pages, page_size, Hkv):
+        raise ValueError("cache shape mismatch")
+    page_table = np.ascontiguousarray(page_table, dtype=np.int32)
+    ctx_lens = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    if page_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("page_table / ctx_lens shape mismatch")
+    max_pages = page_table.shape[1]
+    o = np.empty((B, Hq, d_v), dtype=np.float64)
+    lse = np.empty((B, Hq), dtype=np.float64)
+    ks, vs = _strides(k_cache, 3), _strides(v_cache, 3)
+    rc = lib.oracle_decode_paged(elem, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ks),
+                                 _ptr(vs), num_pages, _ptr(page_table), max_pages,
+                                 _ptr(ctx_lens), page_size, B, Hq, Hkv, d_qk, d_v, block, sink,
+                                 local, int(full), float(scale), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_decode_paged rejected its arguments")
+    return o, lse
