@@ -1,0 +1,206 @@
+"""ctypes binding of libssa.so: argument marshalling only.
+
+Each function here hands torch tensors' device pointers, strides and the
+current HIP stream to the C entry point of the same name; every step of the
+computation runs in the library's HIP kernels. There is no fallback: if the
+library is missing or a tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssa.so")
+
+SSA_F32 = 0
+SSA_BF16 = 1
+
+# Exported symbols, in the order include/ssa.h declares them.
+EXPORTS = ("ssa_prefill", "ssa_decode", "full_attn_decode", "ssa_decode_workspace_size",
+           "ssa_status_string")
+
+
+class SSAError(RuntimeError):
+    """A non-zero ssa_status returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class Pattern(ctypes.Structure):
+    """ssa_pattern: block size b, sink blocks s, local blocks l."""
+    _fields_ = [("block", ctypes.c_int32), ("sink", ctypes.c_int32), ("local", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libssa.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.ssa_prefill.restype = ctypes.c_int
+    lib.ssa_prefill.argtypes = [ctypes.c_int, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                i64p, i64p, i64p, i64p, Pattern, f32, p]
+    lib.ssa_decode.restype = ctypes.c_int
+    lib.ssa_decode.argtypes = [ctypes.c_int, p, p, p, i64p, i64p, p, i32, p, i32, i32, i32, i32, i32,
+                               i32, p, p, p, sz, Pattern, f32, p]
+    lib.full_attn_decode.restype = ctypes.c_int
+    lib.full_attn_decode.argtypes = [ctypes.c_int, p, p, p, i64p, i64p, p, i32, p, i32, i32, i32,
+                                     i32, i32, i32, p, p, p, sz, f32, p]
+    lib.ssa_decode_workspace_size.restype = sz
+    lib.ssa_decode_workspace_size.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32,
+                                              Pattern, ctypes.c_int]
+    lib.ssa_status_string.restype = ctypes.c_char_p
+    lib.ssa_status_string.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ssa_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise SSAError(status, status_string(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SSA_BF16
+    if t.dtype == torch.float32:
+        return SSA_F32
+    raise TypeError(f"SSA kernels take bfloat16 or float32 tensors, got {t.dtype}")
+
+
+def _on_gpu(*tensors: torch.Tensor) -> None:
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("SSA kernels run on the GPU only; got a tensor on " + str(t.device))
+
+
+def _strides3(t: torch.Tensor):
+    if t.stride(-1) != 1:
+        raise ValueError("the head-dim axis must have unit stride")
+    return (ctypes.c_int64 * 3)(*t.stride()[:3])
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, block: int = 128, sink: int = 1,
+            local: int = 7, scale: float | None = None, out: torch.Tensor | None = None,
+            return_lse: bool = False):
+    """ssa_prefill: q [B, N, Hq, d_qk], k [B, N, Hkv, d_qk], v [B, N, Hkv, d_v].
+
+    Returns o [B, N, Hq, d_v] (and lse [B, Hq, N] fp32 when ``return_lse``).
+    The default scale is 1/sqrt(d_qk).
+    """
+    lib = load_library()
+    _on_gpu(q, k, v)
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    B, N, Hq, d_qk = q.shape
+    Hkv, d_v = k.shape[2], v.shape[3]
+    if k.shape != (B, N, Hkv, d_qk) or v.shape != (B, N, Hkv, d_v):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if out is None:
+        out = torch.empty((B, N, Hq, d_v), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, N, Hq, d_v) or out.dtype != q.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    _on_gpu(out)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if return_lse else None
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    _check(lib.ssa_prefill(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, N, Hq, Hkv, d_qk,
+                           d_v, _strides3(q), _strides3(k), _strides3(v), _strides3(out),
+                           Pattern(block, sink, local), float(scale), _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def decode_workspace_size(dtype: torch.dtype, batch: int, heads_q: int, heads_kv: int, d_qk: int,
+                          d_v: int, page_size: int, max_pages: int, *, block: int = 128,
+                          sink: int = 1, local: int = 7, full: bool = False) -> int:
+    """Bytes of workspace ssa_decode (or full_attn_decode, ``full=True``) needs."""
+    code = SSA_BF16 if dtype == torch.bfloat16 else SSA_F32
+    return int(load_library().ssa_decode_workspace_size(code, batch, heads_q, heads_kv, d_qk, d_v,
+                                                        page_size, max_pages,
+                                                        Pattern(block, sink, local), int(full)))
+
+
+def _decode(full: bool, q, k_cache, v_cache, page_table, ctx_lens, *, block, sink, local, scale,
+            out, workspace, return_lse):
+    lib = load_library()
+    _on_gpu(q, k_cache, v_cache, page_table, ctx_lens)
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    if page_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise TypeError("page_table and ctx_lens must be int32")
+    if not (q.is_contiguous() and page_table.is_contiguous() and ctx_lens.is_contiguous()):
+        raise ValueError("q, page_table and ctx_lens must be contiguous")
+    B, Hq, d_qk = q.shape
+    _, page_size, Hkv, d_qk2 = k_cache.shape
+    d_v = v_cache.shape[3]
+    if d_qk2 != d_qk or v_cache.shape[:3] != k_cache.shape[:3]:
+        raise ValueError("cache shape mismatch")
+    if page_table.dim() != 2 or page_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("page_table must be [B, max_pages] and ctx_lens [B]")
+    max_pages = page_table.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, d_v), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, Hq, d_v) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Hq, d_v] tensor of q's dtype")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    need = decode_workspace_size(q.dtype, B, Hq, Hkv, d_qk, d_v, page_size, max_pages, block=block,
+                                 sink=sink, local=local, full=full)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _on_gpu(workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    common = (dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _strides3(k_cache), _strides3(v_cache),
+              _ptr(page_table), max_pages, _ptr(ctx_lens), B, Hq, Hkv, d_qk, d_v, page_size,
+              _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes)
+    if full:
+        _check(lib.full_attn_decode(*common, float(scale), _stream(q.device)))
+    else:
+        _check(lib.ssa_decode(*common, Pattern(block, sink, local), float(scale), _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def decode(q, k_cache, v_cache, page_table, ctx_lens, *, block: int = 128, sink: int = 1,
+           local: int = 7, scale: float | None = None, out=None, workspace=None,
+           return_lse: bool = False):
+    """ssa_decode: q [B, Hq, d_qk]; caches [pages, page_size, Hkv, d]; page_table
+    [B, max_pages] int32; ctx_lens [B] int32 (the new token included)."""
+    return _decode(False, q, k_cache, v_cache, page_table, ctx_lens, block=block, sink=sink,
+                   local=local, scale=scale, out=out, workspace=workspace, return_lse=return_lse)
+
+
+def full_decode(q, k_cache, v_cache, page_table, ctx_lens, *, scale: float | None = None, out=None,
+                workspace=None, return_lse: bool = False):
+    """full_attn_decode: as ``decode`` but attending to the whole context."""
+    return _decode(True, q, k_cache, v_cache, page_table, ctx_lens, block=1, sink=0, local=1,
+                   scale=scale, out=out, workspace=workspace, return_lse=return_lse)

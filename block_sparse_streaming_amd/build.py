@@ -1,0 +1,69 @@
+"""Build the SSA HIP library (libssa.so) in-tree for gfx950.
+
+Every source is compiled with hipcc for gfx950 only; packed-fp32 instructions
+are disabled in device code. Objects are built in parallel and linked into
+``block_sparse_streaming_amd/libssa.so``.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libssa.so")
+SOURCES = ["api.cpp", "prefill.hip", "decode.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found: the SSA library needs ROCm to build")
+    return path
+
+
+def common_flags() -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fno-strict-aliasing",
+            "-Wall", "-Wno-unused-function",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include")]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libssa.so; returns the library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmd = [cc, *common_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        # The host pass does not know the packed-fp32 feature; that note is noise.
+        lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
+        if lines and (verbose or p.returncode):
+            print(f"[{src}]\n" + "\n".join(lines), file=sys.stderr)
+        if p.returncode:
+            failed.append(src)
+    if failed:
+        raise RuntimeError(f"hipcc failed for {failed}")
+    tmp = LIB + ".tmp"
+    subprocess.check_call([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,262 @@
+// C ABI of the SSA library: argument checks, work planning and dispatch.
+// Every check runs on the host before any HIP call, so a rejected call
+// launches nothing and touches no device state.
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "../../include/ssa.h"
+#include "kernels.h"
+
+namespace {
+
+using ssa::DecodeArgs;
+using ssa::DecodePlan;
+using ssa::PrefillArgs;
+
+constexpr int64_t kInt32Max = std::numeric_limits<int32_t>::max();
+// Target number of work-groups for a full-attention decode (8 per CU on 256 CUs).
+constexpr int64_t kFullDecodeTargetWgs = 2048;
+// Attended tokens per split for the windowed (SSA) decode.
+constexpr int64_t kSsaSplitTokens = 128;
+
+bool pattern_ok(const ssa_pattern &p) { return p.block >= 1 && p.sink >= 0 && p.local >= 1; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Strides must be non-negative and keep every row on a 16-byte boundary.
+bool strides_ok(const int64_t *s, int n, int elem_bytes) {
+    if (!s) return false;
+    const int64_t unit = 16 / elem_bytes;
+    for (int i = 0; i < n; ++i)
+        if (s[i] < 0 || s[i] % unit) return false;
+    return true;
+}
+
+int elem_bytes(ssa_dtype t) { return t == SSA_BF16 ? 2 : 4; }
+
+bool dtype_ok(ssa_dtype t) { return t == SSA_F32 || t == SSA_BF16; }
+
+// Work plan of a decode call; false if no compiled kernel fits the shape.
+bool make_plan(ssa_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t d_qk,
+               int32_t d_v, int32_t page_size, int32_t max_pages, const ssa_pattern &pat, bool full,
+               DecodePlan *plan) {
+    const bool bf16 = dtype == SSA_BF16;
+    const int group = heads_q / heads_kv;
+    int chunk;
+    if (ssa::decode_latent_supported(bf16, d_qk, d_v, group)) {
+        plan->kind = ssa::kDecodeLatent;
+        plan->head_chunks = (group + 63) / 64;
+        chunk = 32;
+    } else if (ssa::decode_valu_supported(bf16, d_qk, d_v, group)) {
+        plan->kind = ssa::kDecodeValu;
+        plan->head_chunks = 1;
+        chunk = 64;
+    } else {
+        return false;
+    }
+    const int64_t max_ctx = (int64_t)max_pages * page_size;
+    int64_t split;
+    int64_t max_tokens;
+    if (full) {
+        max_tokens = max_ctx;
+        const int64_t wgs_per_split = (int64_t)batch * heads_kv * plan->head_chunks;
+        split = (max_tokens * wgs_per_split + kFullDecodeTargetWgs - 1) / kFullDecodeTargetWgs;
+        split = split < 256 ? 256 : split;
+    } else {
+        const int64_t window = ((int64_t)pat.sink + pat.local) * pat.block;
+        max_tokens = window < max_ctx ? window : max_ctx;
+        split = kSsaSplitTokens;
+    }
+    split = (split + chunk - 1) / chunk * chunk;
+    if (split > kInt32Max) return false;
+    const int64_t splits = (max_tokens + split - 1) / split;
+    if (splits < 1 || splits > 65535) return false;
+    plan->split_tokens = (int)split;
+    plan->max_splits = (int)splits;
+    return true;
+}
+
+struct WorkspaceLayout {
+    size_t o_bytes, lse_offset, total;
+};
+
+WorkspaceLayout workspace_layout(int32_t batch, int32_t heads_q, int32_t d_v, const DecodePlan &plan) {
+    WorkspaceLayout w;
+    const size_t slots = (size_t)batch * heads_q * plan.max_splits;
+    w.o_bytes = slots * d_v * sizeof(float);
+    w.lse_offset = (w.o_bytes + 255) / 256 * 256;
+    w.total = w.lse_offset + slots * sizeof(float);
+    return w;
+}
+
+ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
+                         const int64_t k_strides[3], const int64_t v_strides[3],
+                         const int32_t *page_table, int32_t max_pages, const int32_t *ctx_lens,
+                         int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                         int32_t page_size, void *o, float *lse, void *workspace,
+                         size_t workspace_bytes, ssa_pattern pattern, float scale, bool full,
+                         hipStream_t stream) {
+    if (!dtype_ok(dtype)) return SSA_ERR_INVALID_ARG;
+    if (batch < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv || d_qk < 1 || d_v < 1 ||
+        page_size < 1 || max_pages < 1)
+        return SSA_ERR_INVALID_ARG;
+    if (!full && !pattern_ok(pattern)) return SSA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return SSA_ERR_INVALID_ARG;
+    const int eb = elem_bytes(dtype);
+    if (!strides_ok(k_strides, 3, eb) || !strides_ok(v_strides, 3, eb)) return SSA_ERR_INVALID_ARG;
+    if (batch == 0) return SSA_OK;
+    if (!q || !k_cache || !v_cache || !page_table || !ctx_lens || !o) return SSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+        return SSA_ERR_INVALID_ARG;
+    if ((d_qk * eb) % 16 || (d_v * eb) % 16) return SSA_ERR_INVALID_ARG;
+
+    DecodePlan plan;
+    if (!make_plan(dtype, batch, heads_q, heads_kv, d_qk, d_v, page_size, max_pages, pattern, full, &plan))
+        return SSA_ERR_UNSUPPORTED;
+    if (plan.kind == ssa::kDecodeLatent) {
+        // The latent kernel reads the value as the first d_v entries of the key row.
+        if (v_cache != k_cache || v_strides[0] != k_strides[0] || v_strides[1] != k_strides[1] ||
+            v_strides[2] != k_strides[2])
+            return SSA_ERR_UNSUPPORTED;
+    }
+    if ((int64_t)batch * heads_q > kInt32Max || (int64_t)heads_kv * plan.head_chunks > 65535 ||
+        batch > 65535 || heads_q > 65535)
+        return SSA_ERR_UNSUPPORTED;
+    const WorkspaceLayout wl = workspace_layout(batch, heads_q, d_v, plan);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < wl.total) return SSA_ERR_WORKSPACE;
+
+    DecodeArgs a;
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    for (int i = 0; i < 3; ++i) {
+        a.ks[i] = k_strides[i];
+        a.vs[i] = v_strides[i];
+    }
+    a.page_table = page_table;
+    a.ctx_lens = ctx_lens;
+    a.max_pages = max_pages;
+    a.page_size = page_size;
+    a.B = batch;
+    a.Hq = heads_q;
+    a.Hkv = heads_kv;
+    a.group = heads_q / heads_kv;
+    a.block = full ? 1 : pattern.block;
+    a.sink = full ? 0 : pattern.sink;
+    a.local = full ? 1 : pattern.local;
+    a.full = full ? 1 : 0;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.o = o;
+    a.lse = lse;
+    a.ws_o = static_cast<float *>(workspace);
+    a.ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + wl.lse_offset);
+    a.plan = plan;
+    return ssa::launch_decode(dtype == SSA_BF16, d_qk, d_v, a, stream) == hipSuccess ? SSA_OK : SSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssa_status ssa_prefill(ssa_dtype dtype, const void *q, const void *k, const void *v, void *o,
+                       float *lse, int32_t batch, int32_t seq_len, int32_t heads_q,
+                       int32_t heads_kv, int32_t d_qk, int32_t d_v, const int64_t q_strides[3],
+                       const int64_t k_strides[3], const int64_t v_strides[3],
+                       const int64_t o_strides[3], ssa_pattern pattern, float scale,
+                       hipStream_t stream) {
+    if (!dtype_ok(dtype)) return SSA_ERR_INVALID_ARG;
+    if (batch < 0 || seq_len < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv || d_qk < 1 ||
+        d_v < 1)
+        return SSA_ERR_INVALID_ARG;
+    if (!pattern_ok(pattern) || !std::isfinite(scale)) return SSA_ERR_INVALID_ARG;
+    const int eb = elem_bytes(dtype);
+    if (!strides_ok(q_strides, 3, eb) || !strides_ok(k_strides, 3, eb) || !strides_ok(v_strides, 3, eb) ||
+        !strides_ok(o_strides, 3, eb))
+        return SSA_ERR_INVALID_ARG;
+    if (batch == 0 || seq_len == 0) return SSA_OK;
+    if (!q || !k || !v || !o) return SSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SSA_ERR_INVALID_ARG;
+    if (!ssa::prefill_supported(dtype == SSA_BF16, d_qk, d_v)) return SSA_ERR_UNSUPPORTED;
+
+    const int64_t qtiles = ((int64_t)seq_len + 127) / 128;
+    const int64_t total = qtiles * heads_q * batch;
+    // a 1-D grid holds fewer than 2^32 work-items: 256 per work-group
+    if (total >= (int64_t(1) << 24)) return SSA_ERR_UNSUPPORTED;
+
+    PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = q_strides[i];
+        a.ks[i] = k_strides[i];
+        a.vs[i] = v_strides[i];
+        a.os[i] = o_strides[i];
+    }
+    a.B = batch;
+    a.N = seq_len;
+    a.Hq = heads_q;
+    a.Hkv = heads_kv;
+    a.group = heads_q / heads_kv;
+    a.block = pattern.block;
+    a.sink = pattern.sink;
+    a.local = pattern.local;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.num_qtiles = (int32_t)qtiles;
+    a.total_wgs = (int32_t)total;
+    return ssa::launch_prefill(dtype == SSA_BF16, d_qk, d_v, a, stream) == hipSuccess ? SSA_OK
+                                                                                     : SSA_ERR_HIP;
+}
+
+ssa_status ssa_decode(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
+                      const int64_t k_strides[3], const int64_t v_strides[3],
+                      const int32_t *page_table, int32_t max_pages, const int32_t *ctx_lens,
+                      int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                      int32_t page_size, void *o, float *lse, void *workspace,
+                      size_t workspace_bytes, ssa_pattern pattern, float scale, hipStream_t stream) {
+    return decode_common(dtype, q, k_cache, v_cache, k_strides, v_strides, page_table, max_pages,
+                         ctx_lens, batch, heads_q, heads_kv, d_qk, d_v, page_size, o, lse, workspace,
+                         workspace_bytes, pattern, scale, false, stream);
+}
+
+ssa_status full_attn_decode(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
+                            const int64_t k_strides[3], const int64_t v_strides[3],
+                            const int32_t *page_table, int32_t max_pages, const int32_t *ctx_lens,
+                            int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t d_qk,
+                            int32_t d_v, int32_t page_size, void *o, float *lse, void *workspace,
+                            size_t workspace_bytes, float scale, hipStream_t stream) {
+    const ssa_pattern unused = {1, 0, 1};
+    return decode_common(dtype, q, k_cache, v_cache, k_strides, v_strides, page_table, max_pages,
+                         ctx_lens, batch, heads_q, heads_kv, d_qk, d_v, page_size, o, lse, workspace,
+                         workspace_bytes, unused, scale, true, stream);
+}
+
+size_t ssa_decode_workspace_size(ssa_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                 int32_t d_qk, int32_t d_v, int32_t page_size, int32_t max_pages,
+                                 ssa_pattern pattern, int full) {
+    if (!dtype_ok(dtype) || batch < 1 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv ||
+        page_size < 1 || max_pages < 1 || d_qk < 1 || d_v < 1)
+        return 0;
+    if (!full && !pattern_ok(pattern)) return 0;
+    DecodePlan plan;
+    if (!make_plan(dtype, batch, heads_q, heads_kv, d_qk, d_v, page_size, max_pages, pattern, full != 0,
+                   &plan))
+        return 0;
+    return workspace_layout(batch, heads_q, d_v, plan).total;
+}
+
+const char *ssa_status_string(ssa_status status) {
+    switch (status) {
+        case SSA_OK: return "SSA_OK";
+        case SSA_ERR_INVALID_ARG: return "SSA_ERR_INVALID_ARG: bad size, stride, pattern, scale or pointer";
+        case SSA_ERR_UNSUPPORTED: return "SSA_ERR_UNSUPPORTED: no compiled kernel for this dtype/shape";
+        case SSA_ERR_WORKSPACE: return "SSA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case SSA_ERR_HIP: return "SSA_ERR_HIP: kernel launch failed";
+    }
+    return "unknown ssa_status";
+}
+
+}  // extern "C"

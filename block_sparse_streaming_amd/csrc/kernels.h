@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssa {
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;              // [B, Hq, N] or null
+    int64_t qs[3], ks[3], vs[3], os[3];  // (batch, token, head) element strides
+    int32_t B, N, Hq, Hkv, group;        // group = Hq / Hkv
+    int32_t block, sink, local;
+    float scale_log2;        // softmax scale * log2(e)
+    int32_t num_qtiles;      // ceil(N / 128)
+    int32_t total_wgs;       // num_qtiles * Hq * B
+};
+
+bool prefill_supported(bool bf16, int d_qk, int d_v);
+hipError_t launch_prefill(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream);
+
+enum DecodeKind { kDecodeValu = 0, kDecodeLatent = 1 };
+
+// How a decode call is cut into work-groups. Computed on the host from shapes
+// only (context lengths live on the device), so the workspace size is known
+// before the call.
+struct DecodePlan {
+    int kind;          // DecodeKind
+    int split_tokens;  // attended tokens per split (multiple of the chunk size)
+    int max_splits;    // splits per (sequence, head) the workspace holds
+    int head_chunks;   // latent kernel: work-groups per kv head (64 heads each)
+};
+
+struct DecodeArgs {
+    const void *q, *kc, *vc;
+    int64_t ks[3], vs[3];          // (page, slot, head) element strides
+    const int32_t *page_table;
+    const int32_t *ctx_lens;
+    int32_t max_pages, page_size;
+    int32_t B, Hq, Hkv, group;
+    int32_t block, sink, local, full;
+    float scale_log2;
+    void *o;
+    float *lse;                     // [B, Hq] or null
+    float *ws_o;                    // [B, Hq, max_splits, d_v]
+    float *ws_lse;                  // [B, Hq, max_splits], log2 domain
+    DecodePlan plan;
+};
+
+bool decode_valu_supported(bool bf16, int d_qk, int d_v, int group);
+bool decode_latent_supported(bool bf16, int d_qk, int d_v, int group);
+hipError_t launch_decode(bool bf16, int d_qk, int d_v, const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace ssa

@@ -1,0 +1,156 @@
+"""Seeded synthetic inputs for the SSA workloads (no attention arithmetic here).
+
+Shared by the tests and the benchmark: both sides of every parity check get
+their bytes from these generators. Values are N(0, 1) drawn in fp32 from a
+seeded torch generator and rounded once to the compute dtype (bf16 by
+round-to-nearest-even). Paged caches deal out a seeded random permutation of
+the physical pages to the sequences in logical order.
+
+Workloads (the pages run the method at b=128, s=1, l=7 over 32K-256K contexts
+and compare decode kernels at 128K; these shapes stand in for their models):
+  1  prefill fp32 : B=1, N=2048,   H=4,  d=64
+  2  prefill bf16 : B=1, N=32768,  H=16, d=128
+  3  decode  bf16 : B=32, 64 query heads on one 576-dim latent KV head (value =
+                    first 512 dims), L=131072 per sequence, 128-token pages
+  4  prefill bf16 : B=1, N=262144, H=64, d_qk=192, d_v=128
+  5  decode  bf16 : 64 sequences, L log-uniform in [4096, 1048576], plus one
+                    sequence with L in [1, 1023]; 16 heads, d=128, 128-token pages
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+PAGE_SIZE = 128
+PATTERN = dict(block=128, sink=1, local=7)
+
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    dtype: torch.dtype
+    B: int
+    N: int
+    Hq: int
+    Hkv: int
+    d_qk: int
+    d_v: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_qk)
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    dtype: torch.dtype
+    Hq: int
+    Hkv: int
+    d_qk: int
+    d_v: int
+    latent: bool                 # value = first d_v entries of the key row
+    seed: int
+    lens: tuple = field(default=())
+
+    @property
+    def B(self) -> int:
+        return len(self.lens)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_qk)
+
+
+def config5_lens(seed: int = 1005) -> tuple:
+    """64 context lengths floor(exp(U(ln 4096, ln 1048576))) plus one in [1, 1023]."""
+    rng = np.random.default_rng(seed)
+    u = rng.uniform(math.log(4096), math.log(1048576), size=64)
+    lens = [int(math.floor(math.exp(x))) for x in u]
+    lens.append(int(rng.integers(1, 1024)))
+    return tuple(lens)
+
+
+CONFIGS = {
+    1: PrefillConfig("prefill_fp32_b1_n2048_h4_d64", torch.float32, 1, 2048, 4, 4, 64, 64, 1001),
+    2: PrefillConfig("prefill_bf16_b1_n32768_h16_d128", torch.bfloat16, 1, 32768, 16, 16, 128, 128, 1002),
+    3: DecodeConfig("decode_bf16_latent_b32_h64_d576_L131072", torch.bfloat16, 64, 1, 576, 512, True,
+                    1003, lens=(131072,) * 32),
+    4: PrefillConfig("prefill_bf16_b1_n262144_h64_dqk192_dv128", torch.bfloat16, 1, 262144, 64, 64,
+                     192, 128, 1004),
+    5: DecodeConfig("decode_bf16_ragged_65seq_h16_d128", torch.bfloat16, 16, 16, 128, 128, False, 1005,
+                    lens=config5_lens()),
+}
+
+
+def randn(shape, dtype: torch.dtype, device, gen: torch.Generator, chunk_elems: int = 1 << 28):
+    """N(0,1) drawn in fp32 and rounded once to ``dtype``; filled in chunks so a
+    huge bf16 tensor never needs an fp32 copy of itself."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    for s in range(0, flat.numel(), chunk_elems):
+        n = min(chunk_elems, flat.numel() - s)
+        flat[s:s + n] = torch.randn(n, generator=gen, device=device, dtype=torch.float32).to(dtype)
+    return out
+
+
+def generator(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def prefill_inputs(cfg: PrefillConfig, device, seed: int | None = None):
+    """q [B, N, Hq, d_qk], k [B, N, Hkv, d_qk], v [B, N, Hkv, d_v]."""
+    gen = generator(device, cfg.seed if seed is None else seed)
+    q = randn((cfg.B, cfg.N, cfg.Hq, cfg.d_qk), cfg.dtype, device, gen)
+    k = randn((cfg.B, cfg.N, cfg.Hkv, cfg.d_qk), cfg.dtype, device, gen)
+    v = randn((cfg.B, cfg.N, cfg.Hkv, cfg.d_v), cfg.dtype, device, gen)
+    return q, k, v
+
+
+def page_table_for(lens, page_size: int, seed: int, spare_pages: int = 0):
+    """Deal a seeded permutation of all physical pages to the sequences.
+
+    Returns (page_table [B, max_pages] int32 numpy, num_pages). Entries past a
+    sequence's last page are 0 (never read)."""
+    pages_per = [max(1, -(-int(L) // page_size)) for L in lens]
+    total = sum(pages_per) + spare_pages
+    perm = np.random.default_rng(seed).permutation(total).astype(np.int32)
+    table = np.zeros((len(lens), max(pages_per)), dtype=np.int32)
+    nxt = 0
+    for b, n in enumerate(pages_per):
+        table[b, :n] = perm[nxt:nxt + n]
+        nxt += n
+    return table, total
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor            # [B, Hq, d_qk]
+    k_cache: torch.Tensor      # [pages, page_size, Hkv, d_qk]
+    v_cache: torch.Tensor      # [pages, page_size, Hkv, d_v] (a view of k_cache when latent)
+    page_table: torch.Tensor   # [B, max_pages] int32
+    ctx_lens: torch.Tensor     # [B] int32
+    table_np: np.ndarray
+    lens: tuple
+
+
+def decode_inputs(cfg: DecodeConfig, device, *, lens=None, seed: int | None = None,
+                  spare_pages: int = 0, page_size: int = PAGE_SIZE) -> DecodeInputs:
+    lens = tuple(cfg.lens if lens is None else lens)
+    seed = cfg.seed if seed is None else seed
+    table, num_pages = page_table_for(lens, page_size, seed, spare_pages)
+    gen = generator(device, seed)
+    q = randn((len(lens), cfg.Hq, cfg.d_qk), cfg.dtype, device, gen)
+    k_cache = randn((num_pages, page_size, cfg.Hkv, cfg.d_qk), cfg.dtype, device, gen)
+    if cfg.latent:
+        v_cache = k_cache[..., :cfg.d_v]
+    else:
+        v_cache = randn((num_pages, page_size, cfg.Hkv, cfg.d_v), cfg.dtype, device, gen)
+    return DecodeInputs(q, k_cache, v_cache, torch.from_numpy(table).to(device),
+                        torch.tensor(lens, dtype=torch.int32, device=device), table, lens)

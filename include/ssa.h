@@ -1,0 +1,162 @@
+/*
+ * ssa.h - C ABI of the streaming sparse attention (SSA) kernel library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (LongCat ZigZag Attention; digest on www.163.com, section 01,
+ * part (1): the SSA paragraph after the calibration equations; part (2): the
+ * deployed configuration): each query token attends only to a few "sink"
+ * blocks and a few "local" blocks; the selected, blocked keys and values are
+ * fixed by the number of sink blocks s, the number of local blocks l and the
+ * block size b. The deployed setting is b = 128, s = 1, l = 7, a 1,024-token
+ * window; the same page's section 02 (efficiency figure paragraph) compares a
+ * streaming sparse decode kernel with a full-attention decode kernel.
+ *
+ * Exact rule implemented (readings of the page, which lost the equation):
+ * blocks are b consecutive positions aligned at 0; for a query at position i
+ * in block qb = i / b, key j is attended iff
+ *     j <= i   and   ( j / b < s   or   j / b > qb - l )
+ * i.e. the first s blocks plus the l blocks ending at the query's own block,
+ * causal, each key once. The result is softmax(scale * q . k_j) weighted sum
+ * of v_j over the attended keys; lse is the natural-log log-sum-exp of the
+ * scaled scores.
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer argument is a DEVICE pointer owned by the caller (q, k, v,
+ *    caches, outputs, page tables, lengths, workspace). The library allocates
+ *    nothing, keeps no pointer after it returns and holds no mutable global
+ *    state; calls on different streams are independent.
+ *  - Calls are asynchronous on `stream`. Inputs, outputs and workspace must
+ *    stay valid until the stream passes the call.
+ *  - Arguments are checked on the host before anything is launched:
+ *    SSA_ERR_INVALID_ARG for a bad size, stride, pattern, scale or pointer;
+ *    SSA_ERR_UNSUPPORTED for a (dtype, d_qk, d_v, group) combination that has
+ *    no compiled kernel; SSA_ERR_WORKSPACE when the workspace is too small.
+ *    Nothing is launched when a check fails. SSA_ERR_HIP reports a failed
+ *    kernel launch.
+ *  - Strides are in ELEMENTS, the head-dim axis has unit stride, and every
+ *    row must start on a 16-byte boundary (pointers and strides aligned).
+ *  - Accumulation is fp32. bf16 outputs are rounded to nearest-even.
+ *  - Device-resident integers (page ids, context lengths) are trusted: they
+ *    are not range-checked on the host.
+ */
+#ifndef BLOCK_SPARSE_STREAMING_SSA_H
+#define BLOCK_SPARSE_STREAMING_SSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssa_status {
+    SSA_OK = 0,
+    SSA_ERR_INVALID_ARG = 1,
+    SSA_ERR_UNSUPPORTED = 2,
+    SSA_ERR_WORKSPACE = 3,
+    SSA_ERR_HIP = 4
+} ssa_status;
+
+/* Element type of q, k, v, caches and outputs (lse is always fp32). */
+typedef enum ssa_dtype { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
+
+/* The SSA pattern: block size b >= 1, sink blocks s >= 0, local blocks l >= 1
+ * (the local blocks include the query's own block, so l >= 1 keeps every row
+ * non-empty). */
+typedef struct ssa_pattern {
+    int32_t block;
+    int32_t sink;
+    int32_t local;
+} ssa_pattern;
+
+/*
+ * ssa_prefill - causal streaming sparse attention over whole sequences
+ * (the SSA operator of the digest's section 01 part (1), applied to every
+ * query row of a sequence, as in prefill).
+ *
+ *   q   [batch, seq_len, heads_q,  d_qk]  strides q_strides  (batch, token, head)
+ *   k   [batch, seq_len, heads_kv, d_qk]  strides k_strides
+ *   v   [batch, seq_len, heads_kv, d_v ]  strides v_strides
+ *   o   [batch, seq_len, heads_q,  d_v ]  strides o_strides, written
+ *   lse [batch, heads_q, seq_len] fp32 contiguous, written; may be NULL
+ * Query head h reads kv head h / (heads_q / heads_kv); heads_q % heads_kv
+ * must be 0. batch == 0 or seq_len == 0 is a no-op returning SSA_OK.
+ * Compiled (dtype, d_qk, d_v): bf16 (64,64), (128,128), (192,128);
+ * fp32 (64,64), (128,128).
+ */
+ssa_status ssa_prefill(ssa_dtype dtype, const void *q, const void *k, const void *v, void *o,
+                       float *lse, int32_t batch, int32_t seq_len, int32_t heads_q,
+                       int32_t heads_kv, int32_t d_qk, int32_t d_v, const int64_t q_strides[3],
+                       const int64_t k_strides[3], const int64_t v_strides[3],
+                       const int64_t o_strides[3], ssa_pattern pattern, float scale,
+                       hipStream_t stream);
+
+/*
+ * ssa_decode - one new query token per sequence against a paged KV cache,
+ * attending to the SSA window (digest section 02: the streaming sparse
+ * attention kernel in the decode phase).
+ *
+ *   q          [batch, heads_q, d_qk] contiguous.
+ *   k_cache    page-major cache; element (page, slot, kv head, dim) sits at
+ *              page*k_strides[0] + slot*k_strides[1] + head*k_strides[2] + dim.
+ *   v_cache    likewise with v_strides and d_v dims. v_cache may equal k_cache
+ *              with equal strides: then the value is the first d_v entries of
+ *              the key row (a latent cache, as in absorbed MLA).
+ *   page_table [batch, max_pages] int32 physical page ids, row-major.
+ *   ctx_lens   [batch] int32 context lengths L, the new token included: its
+ *              key and value are already in the cache and the query sits at
+ *              position L - 1. Token t of a sequence is in page
+ *              page_table[t / page_size] at slot t % page_size.
+ *              L <= 0 writes a zero output and lse = -inf; L must not exceed
+ *              max_pages * page_size.
+ *   o          [batch, heads_q, d_v] contiguous, written; lse [batch, heads_q]
+ *              fp32 or NULL.
+ *   workspace  device scratch of at least ssa_decode_workspace_size(...)
+ *              bytes (same shape arguments, full = 0); no initial contents
+ *              are required. Calls sharing one workspace must not overlap.
+ * Compiled: bf16 or fp32 with d_qk, d_v in {64, 128, 256} and
+ * heads_q / heads_kv in {1, 2, 4, 8}; bf16 latent shape d_qk = 576,
+ * d_v = 512 with heads_q / heads_kv a multiple of 16.
+ */
+ssa_status ssa_decode(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
+                      const int64_t k_strides[3], const int64_t v_strides[3],
+                      const int32_t *page_table, int32_t max_pages, const int32_t *ctx_lens,
+                      int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t d_qk,
+                      int32_t d_v, int32_t page_size, void *o, float *lse, void *workspace,
+                      size_t workspace_bytes, ssa_pattern pattern, float scale,
+                      hipStream_t stream);
+
+/*
+ * full_attn_decode - the dense comparator of the digest's section 02
+ * efficiency figure: the same call as ssa_decode, attending to every token
+ * 0..L-1 of the context. Same layouts, ownership, errors and compiled shapes.
+ */
+ssa_status full_attn_decode(ssa_dtype dtype, const void *q, const void *k_cache,
+                            const void *v_cache, const int64_t k_strides[3],
+                            const int64_t v_strides[3], const int32_t *page_table,
+                            int32_t max_pages, const int32_t *ctx_lens, int32_t batch,
+                            int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                            int32_t page_size, void *o, float *lse, void *workspace,
+                            size_t workspace_bytes, float scale, hipStream_t stream);
+
+/*
+ * Workspace bytes for ssa_decode (full = 0; pattern used) or full_attn_decode
+ * (full = 1; pattern ignored). Returns 0 for arguments the decode calls would
+ * reject. The workspace holds one fp32 partial output and one log-sum-exp per
+ * (sequence, query head, split of the attended tokens).
+ */
+size_t ssa_decode_workspace_size(ssa_dtype dtype, int32_t batch, int32_t heads_q,
+                                 int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                                 int32_t page_size, int32_t max_pages, ssa_pattern pattern,
+                                 int full);
+
+/* Static, human-readable name of a status code. */
+const char *ssa_status_string(ssa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCK_SPARSE_STREAMING_SSA_H */

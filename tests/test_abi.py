@@ -1,0 +1,117 @@
+"""The C ABI on the host: the library loads, exports what include/ssa.h
+declares, and rejects bad arguments before launching anything (every call
+here fails validation or is a no-op, so no GPU is needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import block_sparse_streaming_amd as ssa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ssa.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any launch
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(?:ssa_status|size_t|const char \*)\s*\*?\s*(\w+)\s*\(", text))
+
+
+def test_exports_match_header():
+    lib = ssa.load_library()
+    declared = declared_functions()
+    assert declared == set(ssa.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code, prefix in [(0, "SSA_OK"), (1, "SSA_ERR_INVALID_ARG"), (2, "SSA_ERR_UNSUPPORTED"),
+                         (3, "SSA_ERR_WORKSPACE"), (4, "SSA_ERR_HIP")]:
+        assert ssa.status_string(code).startswith(prefix)
+    assert "unknown" in ssa.status_string(99)
+
+
+def strides(*s):
+    return (ctypes.c_int64 * 3)(*s)
+
+
+def prefill_call(dtype=1, B=1, N=256, Hq=4, Hkv=4, dqk=128, dv=128, pattern=(128, 1, 7),
+                 scale=0.1, ptr=FAKE, qs=None, lse=None):
+    lib = ssa.load_library()
+    st = qs or strides(N * Hq * dqk, Hq * dqk, dqk)
+    p = ctypes.c_void_p(ptr) if ptr is not None else None
+    return lib.ssa_prefill(dtype, p, p, p, p, lse, B, N, Hq, Hkv, dqk, dv, st, st, st, st,
+                           ssa.Pattern(*pattern), scale, None)
+
+
+def test_prefill_validation():
+    assert prefill_call(dtype=7) == INVALID
+    assert prefill_call(B=-1) == INVALID
+    assert prefill_call(Hq=4, Hkv=3) == INVALID
+    assert prefill_call(pattern=(128, 1, 0)) == INVALID     # l = 0 leaves rows empty
+    assert prefill_call(pattern=(0, 1, 7)) == INVALID
+    assert prefill_call(pattern=(128, -1, 7)) == INVALID
+    assert prefill_call(scale=math.nan) == INVALID
+    assert prefill_call(scale=math.inf) == INVALID
+    assert prefill_call(ptr=None) == INVALID
+    assert prefill_call(ptr=FAKE + 2) == INVALID             # misaligned rows
+    assert prefill_call(qs=strides(1024, 3, 1)) == INVALID  # stride not 16-byte aligned
+    assert prefill_call(qs=strides(-8, 8, 8)) == INVALID
+    assert prefill_call(dqk=96, dv=96) == UNSUPPORTED
+    assert prefill_call(dtype=0, dqk=192, dv=128) == UNSUPPORTED
+    # empty problems are no-ops and launch nothing
+    assert prefill_call(B=0, ptr=None) == OK
+    assert prefill_call(N=0, ptr=None) == OK
+
+
+def decode_call(full=False, dtype=1, B=2, Hq=4, Hkv=4, dqk=128, dv=128, ps=128, max_pages=8,
+                pattern=(128, 1, 7), ws_bytes=1 << 30, ptr=FAKE, vptr=None, vs=None):
+    lib = ssa.load_library()
+    ks = strides(ps * Hkv * dqk, Hkv * dqk, dqk)
+    vst = vs or ks
+    p = ctypes.c_void_p(ptr) if ptr is not None else None
+    vp = ctypes.c_void_p(vptr) if vptr is not None else p
+    args = [dtype, p, p, vp, ks, vst, p, max_pages, p, B, Hq, Hkv, dqk, dv, ps, p, None, p, ws_bytes]
+    if full:
+        return lib.full_attn_decode(*args, 0.1, None)
+    return lib.ssa_decode(*args, ssa.Pattern(*pattern), 0.1, None)
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_decode_validation(full):
+    assert decode_call(full, dtype=3) == INVALID
+    assert decode_call(full, Hq=6, Hkv=4) == INVALID
+    assert decode_call(full, ps=0) == INVALID
+    assert decode_call(full, max_pages=0) == INVALID
+    assert decode_call(full, ptr=None) == INVALID
+    assert decode_call(full, ptr=FAKE + 4) == INVALID
+    assert decode_call(full, dqk=96, dv=96) == UNSUPPORTED
+    assert decode_call(full, Hq=48, Hkv=4) == UNSUPPORTED     # group of 12
+    assert decode_call(full, dtype=0, dqk=576, dv=512, Hq=64, Hkv=1) == UNSUPPORTED
+    # the latent kernel needs v_cache to alias k_cache
+    assert decode_call(full, dqk=576, dv=512, Hq=64, Hkv=1, vptr=FAKE + 4096) == UNSUPPORTED
+    assert decode_call(full, ws_bytes=16) == WORKSPACE
+    assert decode_call(full, B=0, ptr=None) == OK
+    if not full:
+        assert decode_call(pattern=(128, 1, 0)) == INVALID
+
+
+def test_workspace_sizes():
+    import torch
+    ws = ssa.decode_workspace_size
+    # windowed decode: (s + l) * b / 128 tokens per split = 8 splits of (d_v + 1) floats
+    slots = 32 * 64 * 8
+    need = ws(torch.bfloat16, 32, 64, 1, 576, 512, 128, 1024)
+    lse_off = -(-slots * 512 * 4 // 256) * 256
+    assert need == lse_off + slots * 4
+    # short caches bound the window: max_pages * page_size = 256 tokens -> 2 splits
+    assert ws(torch.bfloat16, 1, 16, 16, 128, 128, 128, 2) == -(-16 * 2 * 128 * 4 // 256) * 256 + 16 * 2 * 4
+    # full decode grows with the context
+    assert ws(torch.bfloat16, 32, 64, 1, 576, 512, 128, 1024, full=True) > need
+    assert ws(torch.bfloat16, 1, 4, 3, 128, 128, 128, 8) == 0          # invalid heads
+    assert ws(torch.bfloat16, 1, 4, 4, 128, 128, 128, 8, local=0) == 0
