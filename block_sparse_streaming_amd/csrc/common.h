@@ -40,6 +40,57 @@ __device__ __forceinline__ uint32_t pick_pair(const u32x4& a, const u32x4& b, in
     return (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + vmcnt_hi[15:14],
+// expcnt[6:4], lgkmcnt[11:8]); the counters not named are left at their max.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+// Work-group barrier for pipelines that load LDS with direct global->LDS
+// transfers. __syncthreads() carries a fence that waits for every outstanding
+// vector-memory operation, prefetches included; here the caller waits for
+// exactly the transfers it needs (wait_vmcnt) and this barrier only orders
+// the waves. The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void barrier_no_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Barrier after which every wave's LDS reads issued before it have completed,
+// so the buffer they read may be overwritten.
+__device__ __forceinline__ void barrier_lds_drained() {
+    asm volatile("" ::: "memory");
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 16 bytes global -> LDS without passing through registers. Lane i of the wave
+// writes lds_wave_base + 16*i; the base must be the same for the whole wave.
+__device__ __forceinline__ void dma16(const void *src, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_wave_base, 16, 0, 0);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// result lane i, element k is element (i % 4) of the 8 bytes addressed by
+// lane 4k + i/4. If lane s of a group points at row s/4, columns 4(s%4)..+3 of
+// a row-major 4x16 block of 16-bit values, lane i receives column i.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs, each with its own L2.
 // Renumber them so that XCD x runs one contiguous range of logical ids:
 // neighbouring work items then share an L2. A bijection on [0, total).

@@ -7,21 +7,27 @@
 // Design (one work-group = 128 query rows of one head, 4 waves x 32 rows):
 //  * The key set of a query tile is the union of at most two contiguous ranges,
 //    the sink range [0, min(sb, q1)) and the local range [lo(q0), q1); only
-//    these are visited, in 64-key sub-tiles (<= 2*(s+l) sub-tiles per tile for
-//    b = 128), so the work is linear in the sequence length.
+//    these are visited, in 64-key sub-tiles (16 sub-tiles per steady-state
+//    tile at b = 128), so the work is linear in the sequence length.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    in the 32x32 accumulator layout every lane holds ONE query column and 16
 //    keys, so the row max / row sum of the online softmax are per-lane plus a
 //    single exchange between the two half-waves.
 //  * O^T = V^T P^T reuses the score registers directly as the B operand (no
-//    shuffles); V is staged into LDS transposed, with its key order permuted to
-//    match the accumulator layout, so each A-operand fetch is one 16-byte read.
+//    shuffles). V stays row-major in LDS; the A operand is gathered with the
+//    gfx950 LDS transpose read, two 8-byte reads per instruction.
+//  * bf16 K/V sub-tiles are streamed global -> LDS by direct transfers into
+//    two buffers: sub-tile t+1 is in flight while t is computed, and no
+//    registers are spent on staging. Rows are XOR-swizzled in 16-byte units so
+//    that both the score-operand reads (16 keys, one column) and the transpose
+//    reads (4 keys x 64 bytes) hit distinct LDS banks.
 //  * Only sub-tiles that cross a window edge or the diagonal are masked.
 //  * Work-group ids are remapped so that each XCD (own L2) runs a contiguous
 //    run of query tiles of one head: the sink tile and overlapping local tiles
 //    are then L2 hits.
-//  * fp32 inputs take v_mfma_f32_32x32x2f32 (full fp32 products, no xf32); V
-//    then needs no transpose because each lane feeds one key per instruction.
+//  * fp32 inputs take v_mfma_f32_32x32x2f32 (full fp32 products, no xf32) on a
+//    simpler register-staged loop; V then needs no transpose because each lane
+//    feeds one key per instruction.
 #include <type_traits>
 
 #include "common.h"
@@ -34,24 +40,81 @@ constexpr int kBM = 128;      // query rows per work-group
 constexpr int kBN = 64;       // keys per sub-tile
 constexpr int kThreads = 256;
 
-// Position of key kk (0..63) of a sub-tile inside a V^T row: bits 2 and 3 are
-// swapped so that the 8 keys one lane feeds to one P.V instruction (4 keys of
-// its half-wave from each of two 4-row groups of the accumulator) are adjacent.
-__device__ __forceinline__ int vt_quad_pos(int quad) {
-    return 4 * ((quad & ~3) | ((quad & 1) << 1) | ((quad >> 1) & 1));
+// Shared geometry of a query tile: its two key ranges and mask bounds. All
+// positions fit in int32 (seq_len is an int32); bounds are clamped to [0, N].
+struct TileRanges {
+    int q0, q1, sb, sink_end, loc_begin, lo_last;
+    int n_sink, n_total;  // sub-tiles in the sink range, in both ranges
+};
+
+// First key of the local window of query position q (block rule), in [0, N].
+__device__ __forceinline__ int local_start(const PrefillArgs &a, int64_t q) {
+    const int64_t lo = (q / a.block - a.local + 1) * (int64_t)a.block;
+    return (int)(lo < 0 ? 0 : (lo > a.N ? a.N : lo));
 }
 
-template <bool kBF16, int DQK, int DV>
-__global__ __launch_bounds__(kThreads, 2) void ssa_prefill_kernel(const PrefillArgs a) {
-    using Elem = std::conditional_t<kBF16, uint16_t, float>;
-    // LDS: K tile row-major (one row per key); V^T (bf16: one row per value dim)
-    // or V row-major (fp32). Rows are padded by 16 bytes against bank conflicts.
-    constexpr int KSTR = kBF16 ? DQK + 8 : DQK + 4;
-    constexpr int VSTR = kBF16 ? kBN + 8 : DV + 4;
-    constexpr int VROWS = kBF16 ? DV : kBN;
-    constexpr int NDB = DV / 32;  // 32-wide output blocks
-    __shared__ __attribute__((aligned(16))) Elem k_lds[kBN * KSTR];
-    __shared__ __attribute__((aligned(16))) Elem v_lds[VROWS * VSTR];
+__device__ __forceinline__ TileRanges tile_ranges(const PrefillArgs &a, int qt) {
+    TileRanges r;
+    const int N = a.N;
+    const int64_t sb = (int64_t)a.sink * a.block;
+    r.sb = (int)(sb < N ? sb : N);
+    r.q0 = qt * kBM;
+    r.q1 = r.q0 + kBM < N ? r.q0 + kBM : N;
+    const int lo_first = local_start(a, r.q0);
+    r.lo_last = local_start(a, r.q1 - 1);
+    r.sink_end = r.sb < r.q1 ? r.sb : r.q1;
+    r.loc_begin = lo_first > r.sink_end ? lo_first : r.sink_end;
+    r.n_sink = (r.sink_end + kBN - 1) / kBN;
+    r.n_total = r.n_sink + (r.q1 - r.loc_begin + kBN - 1) / kBN;
+    return r;
+}
+
+// Sub-tile t of a tile: first key, end of its range, and whether any pair in
+// it can be masked (it crosses a range end, the diagonal of the tile's first
+// row or, in the local range, the window start of the tile's last row).
+struct SubTile {
+    int j0, re;
+    bool need_mask;
+};
+
+__device__ __forceinline__ SubTile sub_tile(const TileRanges &r, int t) {
+    SubTile s;
+    const bool local = t >= r.n_sink;
+    s.j0 = local ? r.loc_begin + (t - r.n_sink) * kBN : t * kBN;
+    s.re = local ? r.q1 : r.sink_end;
+    s.need_mask = !((s.j0 + kBN <= s.re) && (s.j0 + kBN - 1 <= r.q0) && (!local || s.j0 >= r.lo_last));
+    return s;
+}
+
+// ---------------------------------------------------------------------------
+// bf16: pipelined direct-to-LDS kernel.
+// ---------------------------------------------------------------------------
+// XOR swizzle of the 16-byte column unit of K row `row` (CK units per row):
+// 16 consecutive rows read at one column land in 16 distinct bank groups.
+template <int CK>
+__device__ __forceinline__ int k_swz(int row) {
+    if constexpr (CK % 16 == 0) return row & 15;  // rows a multiple of 256 B
+    else return (row >> 1) & 7;                   // rows 128 B mod 256 B
+}
+// XOR swizzle of V rows: 4 consecutive rows x 4 consecutive units (one
+// transpose read of a half-wave) land in 16 distinct bank groups.
+template <int CV>
+__device__ __forceinline__ int v_swz(int row) {
+    if constexpr (CV % 16 == 0) return 4 * (row & 3);
+    else return 4 * ((row >> 1) & 1);
+}
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArgs a) {
+    constexpr int CK = DQK / 8, CV = DV / 8;   // 16-byte units per K / V row
+    constexpr int NIK = CK / 4, NIV = CV / 4;  // direct transfers per wave per sub-tile
+    constexpr int NDMA = NIK + NIV;
+    constexpr int NQ = DQK / 16, NDB = DV / 32;
+    static_assert(CK % 4 == 0 && CV % 4 == 0, "tile rows must split into whole waves");
+    __shared__ __attribute__((aligned(1024))) uint16_t k_buf0[kBN * DQK];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_buf1[kBN * DQK];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_buf0[kBN * DV];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_buf1[kBN * DV];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -62,36 +125,268 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_kernel(const PrefillA
     const int h = hb % a.Hq, bb = hb / a.Hq;
     const int g = h / a.group;
 
-    const int64_t N = a.N, b = a.block;
-    const int64_t sb = (int64_t)a.sink * b;
-    const int64_t q0 = (int64_t)qt * kBM;
-    const int64_t q1 = q0 + kBM < N ? q0 + kBM : N;
-    const int64_t i = q0 + wave * 32 + l32;  // this lane's query row
-    const bool row_ok = i < N;
-    const int64_t lo_i = (i / b - a.local + 1) * b;  // first local key of row i
-    const int64_t lo_first = (q0 / b - a.local + 1) * b;
-    const int64_t lo_last = ((q1 - 1) / b - a.local + 1) * b;
-    const int64_t sink_end = sb < q1 ? sb : q1;
-    const int64_t loc_begin = lo_first > sink_end ? lo_first : sink_end;
+    const TileRanges tr = tile_ranges(a, qt);
+    const int i = tr.q0 + wave * 32 + l32;  // this lane's query row
+    const bool row_ok = i < a.N;
+    const int lo_i = local_start(a, i);
 
-    const Elem *qbase = (const Elem *)a.q + bb * a.qs[0] + h * a.qs[2];
-    const Elem *kbase = (const Elem *)a.k + bb * a.ks[0] + g * a.ks[2];
-    const Elem *vbase = (const Elem *)a.v + bb * a.vs[0] + g * a.vs[2];
+    const uint16_t *qbase = (const uint16_t *)a.q + bb * a.qs[0] + h * a.qs[2];
+    const uint16_t *kbase = (const uint16_t *)a.k + bb * a.ks[0] + g * a.ks[2];
+    const uint16_t *vbase = (const uint16_t *)a.v + bb * a.vs[0] + g * a.vs[2];
+    const int ks1 = (int)a.ks[1], vs1 = (int)a.vs[1];  // token strides (< 2^24, host-checked)
 
     // Q^T operand, resident in registers for the whole tile.
-    constexpr int NQ = kBF16 ? DQK / 16 : DQK / 2;
-    using QFrag = std::conditional_t<kBF16, bf16x8, float>;
-    QFrag qf[NQ];
-    if constexpr (kBF16) {
-        const Elem *qrow = qbase + i * a.qs[1] + 8 * hi;
+    bf16x8 qf[NQ];
+    {
+        const uint16_t *qrow = qbase + (int64_t)i * a.qs[1] + 8 * hi;
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks) {
             u32x4 w = {0u, 0u, 0u, 0u};
             if (row_ok) w = *(const u32x4 *)(qrow + ks * 16);
             qf[ks] = __builtin_bit_cast(bf16x8, w);
         }
-    } else {
-        const Elem *qrow = qbase + i * a.qs[1] + hi;
+    }
+
+    // Direct transfers: lane slot p of transfer n covers tile row p / C at
+    // physical unit p % C, which holds logical unit (p % C) ^ swz(row). Byte
+    // offsets from the sub-tile's first row; rows past the range end re-read
+    // the range's last row (masked later), so nothing outside the tile's
+    // attended key set is touched.
+    auto dma_off = [&](int p, int C, int swz, int stride, int rows_valid) -> uint32_t {
+        int row = p / C;
+        const int unit = (p % C) ^ swz;
+        row = row < rows_valid ? row : rows_valid - 1;
+        return (uint32_t)(row * stride + unit * 8) * 2u;
+    };
+    auto issue = [&](int t, uint16_t *kb, uint16_t *vb) {
+        const SubTile st = sub_tile(tr, t);
+        const int rows_valid = st.re - st.j0;
+        const char *kt = (const char *)(kbase + (int64_t)st.j0 * a.ks[1]);
+        const char *vt = (const char *)(vbase + (int64_t)st.j0 * a.vs[1]);
+#pragma unroll
+        for (int n = 0; n < NIK; ++n) {
+            const int p = (wave * NIK + n) * 64 + lane;
+            dma16(kt + dma_off(p, CK, k_swz<CK>(p / CK), ks1, rows_valid), kb + (wave * NIK + n) * 512);
+        }
+#pragma unroll
+        for (int n = 0; n < NIV; ++n) {
+            const int p = (wave * NIV + n) * 64 + lane;
+            dma16(vt + dma_off(p, CV, v_swz<CV>(p / CV), vs1, rows_valid), vb + (wave * NIV + n) * 512);
+        }
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
+
+    // LDS byte offsets that depend only on the lane.
+    // K (score operand): row l32 (+32 per key block), unit (2ks + hi) ^ swz;
+    // since 2ks and hi occupy different bits, unit*16 = (32ks) ^ kz.
+    const uint32_t k_lane = (uint32_t)l32 * (DQK * 2);
+    const uint32_t kz = (uint32_t)((hi ^ k_swz<CK>(l32)) << 4);
+    // V (transpose reads): lane s of 16-lane group G reads key row
+    // 4*hi + s/4 (+ block offsets) at value column 16*(G&1) + 4*(s&3) + 32d.
+    // The row swizzle depends only on s, so the physical unit of column block
+    // d is 4*(d ^ y) + x and each block's address is a lane constant.
+    const int grp = lane >> 4, s16 = lane & 15;
+    const int tr_row = 4 * hi + (s16 >> 2);
+    const int tr_col = 16 * (grp & 1) + 4 * (s16 & 3);
+    const int vy = v_swz<CV>(tr_row) >> 2;
+    uint32_t v_lane[NDB];
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+        v_lane[d] = (uint32_t)tr_row * (DV * 2) + (uint32_t)((4 * (d ^ vy) + (tr_col >> 3)) << 4) +
+                    (uint32_t)((tr_col & 4) << 1);
+    const int jl = 4 * hi;  // key offset of this lane's accumulator rows
+
+    auto compute = [&](int t, const uint16_t *kb, const uint16_t *vb) {
+        const SubTile st = sub_tile(tr, t);
+        // Re-derive the lane offsets here (the empty asm hides their origin)
+        // so that address arithmetic is not hoisted out of the loop into
+        // registers that would stay live across it.
+        uint32_t kl = k_lane, kzz = kz;
+        asm volatile("" : "+v"(kl), "+v"(kzz));
+        uint32_t vl[NDB];
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+            vl[d] = v_lane[d];
+            asm volatile("" : "+v"(vl[d]));
+        }
+        const char *kc = (const char *)kb + kl;
+        const char *vc = (const char *)vb;
+        // S^T = K Q^T for two 32-key blocks: accumulator element r of lane
+        // (l32, hi) is key 8*(r/4) + 4*hi + r%4 of the block, query l32.
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kbk][r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < NQ; ++ks) {
+                const uint32_t off = kbk * 32 * DQK * 2 + (((uint32_t)(32 * (ks & 7)) ^ kzz) + (ks >> 3) * 256);
+                const bf16x8 kf = *(const bf16x8 *)(kc + off);
+                sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kbk], 0, 0, 0);
+            }
+        }
+
+        // Online softmax in base 2 (scores pre-multiplied by scale*log2 e).
+        float mx = -INFINITY;
+        if (st.need_mask) {
+            const int jb = st.j0 + jl;
+#pragma unroll
+            for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = jb + kbk * 32 + 8 * (r >> 2) + (r & 3);
+                    const bool ok = (j < st.re) & (j <= i) & ((j < tr.sb) | (j >= lo_i));
+                    const float x = ok ? sacc[kbk][r] * a.scale_log2 : -INFINITY;
+                    sacc[kbk][r] = x;
+                    mx = fmaxf(mx, x);
+                }
+        } else {
+#pragma unroll
+            for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float x = sacc[kbk][r] * a.scale_log2;
+                    sacc[kbk][r] = x;
+                    mx = fmaxf(mx, x);
+                }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float rs = 0.f;
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(sacc[kbk][r] - m_use);
+                sacc[kbk][r] = p;
+                rs += p;
+            }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+        // Rescale only when some lane's running max moved.
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int d = 0; d < NDB; ++d)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+        }
+
+        // O^T += V^T P^T. Instruction c of key block kbk consumes keys
+        // kbk*32 + 16c + {0..3, 8..11} (+4 on the upper half-wave): exactly the
+        // accumulator elements 8c..8c+7 of the score block.
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4 pw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    pw[e] = pack_bf16x2(sacc[kbk][8 * c + 2 * e], sacc[kbk][8 * c + 2 * e + 1]);
+                const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+                constexpr int kRowBytes = DV * 2;
+                const uint32_t blk = (uint32_t)(kbk * 32 + 16 * c) * kRowBytes;
+#pragma unroll
+                for (int d = 0; d < NDB; ++d) {
+                    const i16x4 lo = lds_read_tr16(vc + vl[d] + blk);
+                    const i16x4 up = lds_read_tr16(vc + vl[d] + blk + 8 * kRowBytes);
+                    const i16x8 v8 = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+                    oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pf,
+                                                                      oacc[d], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Two-stage pipeline: sub-tile t+1 streams into the other buffer while t
+    // is computed. Buffers are separate LDS objects so the compiler can tell
+    // the in-flight transfers from the buffer being read; the steady-state loop
+    // issues and waits unconditionally and the last one or two sub-tiles are
+    // peeled, so every wait is a fixed count.
+    const int T = tr.n_total;
+    int t = 0;
+    if (T > 0) issue(0, k_buf0, v_buf0);
+    for (; t + 2 < T; t += 2) {
+        issue(t + 1, k_buf1, v_buf1);
+        wait_vmcnt<NDMA>();
+        barrier_no_fence();
+        compute(t, k_buf0, v_buf0);
+        barrier_lds_drained();
+        issue(t + 2, k_buf0, v_buf0);
+        wait_vmcnt<NDMA>();
+        barrier_no_fence();
+        compute(t + 1, k_buf1, v_buf1);
+        barrier_lds_drained();
+    }
+    if (t + 1 < T) {
+        issue(t + 1, k_buf1, v_buf1);
+        wait_vmcnt<NDMA>();
+        barrier_no_fence();
+        compute(t, k_buf0, v_buf0);
+        wait_vmcnt<0>();
+        barrier_no_fence();
+        compute(t + 1, k_buf1, v_buf1);
+    } else if (t < T) {
+        wait_vmcnt<0>();
+        barrier_no_fence();
+        compute(t, k_buf0, v_buf0);
+    }
+
+    // Epilogue: O = O / l, lse = ln 2 * (m + log2 l).
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = 1.f / l_tot;
+    if (row_ok) {
+        uint16_t *orow = (uint16_t *)a.o + bb * a.os[0] + (int64_t)i * a.os[1] + h * a.os[2];
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int col = d * 32 + 8 * rq + 4 * hi;
+                *(u32x2 *)(orow + col) =
+                    u32x2{pack_bf16x2(oacc[d][4 * rq] * inv, oacc[d][4 * rq + 1] * inv),
+                          pack_bf16x2(oacc[d][4 * rq + 2] * inv, oacc[d][4 * rq + 3] * inv)};
+            }
+        if (a.lse && hi == 0) a.lse[((int64_t)bb * a.Hq + h) * a.N + i] = (m_run + log2f(l_tot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32: register-staged kernel on the fp32 MFMA.
+// ---------------------------------------------------------------------------
+template <int DQK, int DV>
+__global__ __launch_bounds__(kThreads, 2) void ssa_prefill_f32(const PrefillArgs a) {
+    constexpr int KSTR = DQK + 4, VSTR = DV + 4;  // padded rows (floats)
+    constexpr int NQ = DQK / 2, NDB = DV / 32;
+    __shared__ __attribute__((aligned(16))) float k_lds[kBN * KSTR];
+    __shared__ __attribute__((aligned(16))) float v_lds[kBN * VSTR];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int wg = xcd_remap(blockIdx.x, a.total_wgs);
+    const int qt = wg % a.num_qtiles;
+    const int hb = wg / a.num_qtiles;
+    const int h = hb % a.Hq, bb = hb / a.Hq;
+    const int g = h / a.group;
+
+    const TileRanges tr = tile_ranges(a, qt);
+    const int i = tr.q0 + wave * 32 + l32;
+    const bool row_ok = i < a.N;
+    const int lo_i = local_start(a, i);
+
+    const float *qbase = (const float *)a.q + bb * a.qs[0] + h * a.qs[2];
+    const float *kbase = (const float *)a.k + bb * a.ks[0] + g * a.ks[2];
+    const float *vbase = (const float *)a.v + bb * a.vs[0] + g * a.vs[2];
+
+    float qf[NQ];
+    {
+        const float *qrow = qbase + (int64_t)i * a.qs[1] + hi;
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks) qf[ks] = row_ok ? qrow[2 * ks] : 0.f;
     }
@@ -103,185 +398,102 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_kernel(const PrefillA
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
 
-    for (int rg = 0; rg < 2; ++rg) {
-        const int64_t ra = rg == 0 ? 0 : loc_begin;
-        const int64_t re = rg == 0 ? sink_end : q1;
-        for (int64_t j0 = ra; j0 < re; j0 += kBN) {
-            // A sub-tile needs no mask when it lies inside its range, below the
-            // diagonal of the tile's first row and, for the local range, above
-            // the window start of the tile's last row.
-            const bool need_mask =
-                !((j0 + kBN <= re) && (j0 + kBN - 1 <= q0) && (rg == 0 || j0 >= lo_last));
-
-            // Keys past the range end are zero-filled, never read: nothing outside
-            // the tile's attended set (re <= q1 <= N) reaches the arithmetic.
-            __syncthreads();  // previous sub-tile fully consumed
-            if constexpr (kBF16) {
-                constexpr int KCH = DQK / 8;
-#pragma unroll
-                for (int c = tid; c < kBN * KCH; c += kThreads) {
-                    const int row = c / KCH, col = c % KCH;
-                    const int64_t j = j0 + row;
-                    u32x4 w = {0u, 0u, 0u, 0u};
-                    if (j < re) w = *(const u32x4 *)(kbase + j * a.ks[1] + col * 8);
-                    *(u32x4 *)(k_lds + row * KSTR + col * 8) = w;
-                }
-                constexpr int VCH = DV / 8;
-                constexpr int UNITS = (kBN / 4) * VCH;
-#pragma unroll
-                for (int u = tid; u < UNITS; u += kThreads) {
-                    const int dc = u % VCH, quad = u / VCH;
-                    u32x4 rows[4];
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const int64_t j = j0 + 4 * quad + rr;
-                        rows[rr] = u32x4{0u, 0u, 0u, 0u};
-                        if (j < re) rows[rr] = *(const u32x4 *)(vbase + j * a.vs[1] + dc * 8);
-                    }
-                    const int pos = vt_quad_pos(quad);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        u32x2 w2 = {pick_pair(rows[0], rows[1], e), pick_pair(rows[2], rows[3], e)};
-                        *(u32x2 *)(v_lds + (dc * 8 + e) * VSTR + pos) = w2;
-                    }
-                }
-            } else {
-                constexpr int KCH = DQK / 4;
-#pragma unroll
-                for (int c = tid; c < kBN * KCH; c += kThreads) {
-                    const int row = c / KCH, col = c % KCH;
-                    const int64_t j = j0 + row;
-                    f32x4 w = {0.f, 0.f, 0.f, 0.f};
-                    if (j < re) w = *(const f32x4 *)(kbase + j * a.ks[1] + col * 4);
-                    *(f32x4 *)(k_lds + row * KSTR + col * 4) = w;
-                }
-                constexpr int VCH = DV / 4;
-#pragma unroll
-                for (int c = tid; c < kBN * VCH; c += kThreads) {
-                    const int row = c / VCH, col = c % VCH;
-                    const int64_t j = j0 + row;
-                    f32x4 w = {0.f, 0.f, 0.f, 0.f};
-                    if (j < re) w = *(const f32x4 *)(vbase + j * a.vs[1] + col * 4);
-                    *(f32x4 *)(v_lds + row * VSTR + col * 4) = w;
-                }
-            }
-            __syncthreads();
-
-            // S^T = K Q^T for two 32-key blocks. Accumulator element r of lane
-            // (l32, hi) is key 8*(r/4) + 4*hi + r%4 of the block, query l32.
-            f32x16 sacc[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-                const Elem *krow = k_lds + (kb * 32 + l32) * KSTR;
-#pragma unroll
-                for (int ks = 0; ks < NQ; ++ks) {
-                    if constexpr (kBF16) {
-                        const bf16x8 kf = *(const bf16x8 *)(krow + ks * 16 + 8 * hi);
-                        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[kb], 0, 0, 0);
-                    } else {
-                        const float kf = krow[2 * ks + hi];
-                        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf, qf[ks], sacc[kb], 0, 0, 0);
-                    }
-                }
-            }
-
-            // Online softmax in base 2 (scores pre-multiplied by scale*log2 e).
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = sacc[kb][r] * a.scale_log2;
-                    if (need_mask) {
-                        const int64_t j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        const bool ok = (j < re) && (j <= i) && (j < sb || j >= lo_i);
-                        x = ok ? x : -INFINITY;
-                    }
-                    sacc[kb][r] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
-            float rs = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(sacc[kb][r] - m_use);
-                    sacc[kb][r] = p;
-                    rs += p;
-                }
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
-#pragma unroll
-            for (int d = 0; d < NDB; ++d)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-
-            // O^T += V^T P^T.
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if constexpr (kBF16) {
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        u32x4 pw;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            pw[e] = pack_bf16x2(sacc[kb][8 * c + 2 * e], sacc[kb][8 * c + 2 * e + 1]);
-                        const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-                        for (int d = 0; d < NDB; ++d) {
-                            const bf16x8 vf = *(const bf16x8 *)(v_lds + (d * 32 + l32) * VSTR + kb * 32 +
-                                                                16 * c + 8 * hi);
-                            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[d], 0, 0, 0);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-#pragma unroll
-                        for (int d = 0; d < NDB; ++d) {
-                            const float vf = v_lds[key * VSTR + d * 32 + l32];
-                            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf, sacc[kb][r], oacc[d], 0, 0, 0);
-                        }
-                    }
-                }
-            }
+    for (int t = 0; t < tr.n_total; ++t) {
+        const SubTile st = sub_tile(tr, t);
+        __syncthreads();
+        // Keys past the range end are zero-filled, never read.
+        constexpr int KCH = DQK / 4, VCH = DV / 4;
+        for (int c = tid; c < kBN * KCH; c += kThreads) {
+            const int row = c / KCH, col = c % KCH;
+            const int j = st.j0 + row;
+            f32x4 w = {0.f, 0.f, 0.f, 0.f};
+            if (j < st.re) w = *(const f32x4 *)(kbase + (int64_t)j * a.ks[1] + col * 4);
+            *(f32x4 *)(k_lds + row * KSTR + col * 4) = w;
         }
+        for (int c = tid; c < kBN * VCH; c += kThreads) {
+            const int row = c / VCH, col = c % VCH;
+            const int j = st.j0 + row;
+            f32x4 w = {0.f, 0.f, 0.f, 0.f};
+            if (j < st.re) w = *(const f32x4 *)(vbase + (int64_t)j * a.vs[1] + col * 4);
+            *(f32x4 *)(v_lds + row * VSTR + col * 4) = w;
+        }
+        __syncthreads();
+
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kbk][r] = 0.f;
+            const float *krow = k_lds + (kbk * 32 + l32) * KSTR;
+#pragma unroll
+            for (int ks = 0; ks < NQ; ++ks)
+                sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks + hi], qf[ks], sacc[kbk], 0, 0, 0);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = sacc[kbk][r] * a.scale_log2;
+                if (st.need_mask) {
+                    const int j = st.j0 + kbk * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const bool ok = (j < st.re) & (j <= i) & ((j < tr.sb) | (j >= lo_i));
+                    x = ok ? x : -INFINITY;
+                }
+                sacc[kbk][r] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float rs = 0.f;
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(sacc[kbk][r] - m_use);
+                sacc[kbk][r] = p;
+                rs += p;
+            }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kbk * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+#pragma unroll
+                for (int d = 0; d < NDB; ++d)
+                    oacc[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(v_lds[key * VSTR + d * 32 + l32], sacc[kbk][r],
+                                                                   oacc[d], 0, 0, 0);
+            }
     }
 
-    // Epilogue: O = O / l, lse = ln 2 * (m + log2 l).
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.f / l_tot;
     if (row_ok) {
-        Elem *orow = (Elem *)a.o + bb * a.os[0] + i * a.os[1] + h * a.os[2];
+        float *orow = (float *)a.o + bb * a.os[0] + (int64_t)i * a.os[1] + h * a.os[2];
 #pragma unroll
         for (int d = 0; d < NDB; ++d)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 const int col = d * 32 + 8 * rq + 4 * hi;
-                const float v0 = oacc[d][4 * rq + 0] * inv, v1 = oacc[d][4 * rq + 1] * inv;
-                const float v2 = oacc[d][4 * rq + 2] * inv, v3 = oacc[d][4 * rq + 3] * inv;
-                if constexpr (kBF16) {
-                    *(u32x2 *)(orow + col) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-                } else {
-                    *(f32x4 *)(orow + col) = f32x4{v0, v1, v2, v3};
-                }
+                *(f32x4 *)(orow + col) = f32x4{oacc[d][4 * rq] * inv, oacc[d][4 * rq + 1] * inv,
+                                               oacc[d][4 * rq + 2] * inv, oacc[d][4 * rq + 3] * inv};
             }
-        if (a.lse && hi == 0) a.lse[((int64_t)bb * a.Hq + h) * N + i] = (m_run + log2f(l_tot)) * kLn2;
+        if (a.lse && hi == 0) a.lse[((int64_t)bb * a.Hq + h) * a.N + i] = (m_run + log2f(l_tot)) * kLn2;
     }
 }
 
-template <bool kBF16, int DQK, int DV>
-hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
+template <typename K>
+hipError_t launch(K kernel, const PrefillArgs &a, hipStream_t stream) {
     void *args[] = {(void *)&a};
-    return hipLaunchKernel((const void *)ssa_prefill_kernel<kBF16, DQK, DV>, dim3(a.total_wgs),
-                           dim3(kThreads), args, 0, stream);
+    return hipLaunchKernel((const void *)kernel, dim3(a.total_wgs), dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace
@@ -293,12 +505,12 @@ bool prefill_supported(bool bf16, int d_qk, int d_v) {
 
 hipError_t launch_prefill(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream) {
     if (bf16) {
-        if (d_qk == 64 && d_v == 64) return launch<true, 64, 64>(a, stream);
-        if (d_qk == 128 && d_v == 128) return launch<true, 128, 128>(a, stream);
-        if (d_qk == 192 && d_v == 128) return launch<true, 192, 128>(a, stream);
+        if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_bf16<64, 64>, a, stream);
+        if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_bf16<128, 128>, a, stream);
+        if (d_qk == 192 && d_v == 128) return launch(ssa_prefill_bf16<192, 128>, a, stream);
     } else {
-        if (d_qk == 64 && d_v == 64) return launch<false, 64, 64>(a, stream);
-        if (d_qk == 128 && d_v == 128) return launch<false, 128, 128>(a, stream);
+        if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_f32<64, 64>, a, stream);
+        if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_f32<128, 128>, a, stream);
     }
     return hipErrorInvalidValue;
 }
