@@ -5,7 +5,7 @@
 #include <cstdint>
 #include <limits>
 
-#include "../../include/ssa.h"
+#include "ssa.h"
 #include "kernels.h"
 
 namespace {
@@ -102,7 +102,7 @@ ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, co
         page_size < 1 || max_pages < 1)
         return SSA_ERR_INVALID_ARG;
     if (!full && !pattern_ok(pattern)) return SSA_ERR_INVALID_ARG;
-    if (!std::isfinite(scale)) return SSA_ERR_INVALID_ARG;
+    if (!(std::isfinite(scale) && scale > 0.f)) return SSA_ERR_INVALID_ARG;
     const int eb = elem_bytes(dtype);
     if (!strides_ok(k_strides, 3, eb) || !strides_ok(v_strides, 3, eb)) return SSA_ERR_INVALID_ARG;
     if (batch == 0) return SSA_OK;
@@ -169,7 +169,7 @@ ssa_status ssa_prefill(ssa_dtype dtype, const void *q, const void *k, const void
     if (batch < 0 || seq_len < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv || d_qk < 1 ||
         d_v < 1)
         return SSA_ERR_INVALID_ARG;
-    if (!pattern_ok(pattern) || !std::isfinite(scale)) return SSA_ERR_INVALID_ARG;
+    if (!pattern_ok(pattern) || !(std::isfinite(scale) && scale > 0.f)) return SSA_ERR_INVALID_ARG;
     const int eb = elem_bytes(dtype);
     if (!strides_ok(q_strides, 3, eb) || !strides_ok(k_strides, 3, eb) || !strides_ok(v_strides, 3, eb) ||
         !strides_ok(o_strides, 3, eb))
@@ -178,6 +178,11 @@ ssa_status ssa_prefill(ssa_dtype dtype, const void *q, const void *k, const void
     if (!q || !k || !v || !o) return SSA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SSA_ERR_INVALID_ARG;
     if (!ssa::prefill_supported(dtype == SSA_BF16, d_qk, d_v)) return SSA_ERR_UNSUPPORTED;
+    // Kernels index positions in int32 and address a 64-key sub-tile with
+    // 32-bit byte offsets from its first row.
+    if (seq_len > kInt32Max - 256 || k_strides[1] >= (int64_t(1) << 24) ||
+        v_strides[1] >= (int64_t(1) << 24))
+        return SSA_ERR_UNSUPPORTED;
 
     const int64_t qtiles = ((int64_t)seq_len + 127) / 128;
     const int64_t total = qtiles * heads_q * batch;

@@ -39,6 +39,9 @@ namespace {
 constexpr int kBM = 128;      // query rows per work-group
 constexpr int kBN = 64;       // keys per sub-tile
 constexpr int kThreads = 256;
+// Growth of a row max (log2 units) tolerated before the accumulators are
+// rescaled; probabilities stay below 2^8, far from fp32/bf16 overflow.
+constexpr float kRescaleSlack = 8.f;
 
 // Shared geometry of a query tile: its two key ranges and mask bounds. All
 // positions fit in int32 (seq_len is an int32); bounds are clamped to [0, N].
@@ -232,7 +235,11 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             }
         }
 
-        // Online softmax in base 2 (scores pre-multiplied by scale*log2 e).
+        // Online softmax in base 2. The max is taken on raw scores (scale > 0),
+        // and p = 2^(s*c - m) is one FMA and one exp. The running max m_run is
+        // only moved when some lane's max grows by more than kRescaleSlack
+        // (in log2 units): until then p <= 2^kRescaleSlack and the O/l rescale
+        // is skipped. O and l always use the same m_run, so O / l is exact.
         float mx = -INFINITY;
         if (st.need_mask) {
             const int jb = st.j0 + jl;
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
                 for (int r = 0; r < 16; ++r) {
                     const int j = jb + kbk * 32 + 8 * (r >> 2) + (r & 3);
                     const bool ok = (j < st.re) & (j <= i) & ((j < tr.sb) | (j >= lo_i));
-                    const float x = ok ? sacc[kbk][r] * a.scale_log2 : -INFINITY;
+                    const float x = ok ? sacc[kbk][r] : -INFINITY;
                     sacc[kbk][r] = x;
                     mx = fmaxf(mx, x);
                 }
@@ -250,34 +257,30 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
 #pragma unroll
             for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float x = sacc[kbk][r] * a.scale_log2;
-                    sacc[kbk][r] = x;
-                    mx = fmaxf(mx, x);
-                }
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kbk][r]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+            l_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < NDB; ++d)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+            m_run = m_new;
+        }
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
         float rs = 0.f;
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(sacc[kbk][r] - m_use);
+                const float p = fast_exp2(__builtin_fmaf(sacc[kbk][r], a.scale_log2, neg_m));
                 sacc[kbk][r] = p;
                 rs += p;
             }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-        // Rescale only when some lane's running max moved.
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-            for (int d = 0; d < NDB; ++d)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-        }
+        l_run += rs;
 
         // O^T += V^T P^T. Instruction c of key block kbk consumes keys
         // kbk*32 + 16c + {0..3, 8..11} (+4 on the upper half-wave): exactly the

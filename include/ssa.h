@@ -27,6 +27,7 @@
  *    state; calls on different streams are independent.
  *  - Calls are asynchronous on `stream`. Inputs, outputs and workspace must
  *    stay valid until the stream passes the call.
+ *  - The softmax scale must be finite and > 0 (1/sqrt(d_qk) is the usual one).
  *  - Arguments are checked on the host before anything is launched:
  *    SSA_ERR_INVALID_ARG for a bad size, stride, pattern, scale or pointer;
  *    SSA_ERR_UNSUPPORTED for a (dtype, d_qk, d_v, group) combination that has

@@ -58,6 +58,8 @@ def test_prefill_validation():
     assert prefill_call(pattern=(128, -1, 7)) == INVALID
     assert prefill_call(scale=math.nan) == INVALID
     assert prefill_call(scale=math.inf) == INVALID
+    assert prefill_call(scale=0.0) == INVALID
+    assert prefill_call(scale=-0.1) == INVALID
     assert prefill_call(ptr=None) == INVALID
     assert prefill_call(ptr=FAKE + 2) == INVALID             # misaligned rows
     assert prefill_call(qs=strides(1024, 3, 1)) == INVALID  # stride not 16-byte aligned

@@ -119,9 +119,18 @@ def test_config4_stratified_sample():
     _run_and_check(q, k, v, inputs.PATTERN, cfg.scale, rows=rows, what=cfg.name)
 
 
-def test_out_of_window_poison_is_ignored():
-    """NaN in every key/value outside a query tile's attended set leaves that
-    tile's output finite and bit-identical."""
+def _attended_union(rows, N, b, s, l):
+    j = np.arange(N)
+    used = np.zeros(N, dtype=bool)
+    for i in rows:
+        used |= (j <= i) & ((j // b < s) | (j // b > i // b - l))
+    return used
+
+
+def test_out_of_window_keys_have_no_effect():
+    """Keys outside a 128-row query block's attended set, perturbed by +-1e4,
+    leave that block's output bit-identical (masked probabilities are exactly
+    zero)."""
     N, H, d, tile = 3000, 2, 128, 17
     pattern = dict(block=128, sink=1, local=7)
     q = _gen((1, N, H, d), torch.bfloat16, 5)
@@ -129,11 +138,27 @@ def test_out_of_window_poison_is_ignored():
     v = _gen((1, N, H, d), torch.bfloat16, 7)
     ref = ssa.prefill(q, k, v, **pattern)
     rows = np.arange(tile * 128, min((tile + 1) * 128, N))
-    j = np.arange(N)
-    used = np.zeros(N, dtype=bool)
-    for i in rows:
-        used |= (j <= i) & ((j // 128 < 1) | (j // 128 > i // 128 - 7))
-    bad = torch.from_numpy(~used).to(DEV)
+    bad = torch.from_numpy(~_attended_union(rows, N, 128, 1, 7)).to(DEV)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, bad] += 1e4
+    v2[:, bad] -= 1e4
+    got = ssa.prefill(q, k2, v2, **pattern)
+    sl = slice(int(rows[0]), int(rows[-1]) + 1)
+    assert torch.equal(got[:, sl], ref[:, sl])
+
+
+def test_keys_outside_every_window_are_never_read():
+    """NaN in every key/value outside the attended sets of a 256-row span of
+    queries leaves those rows finite and bit-identical: such keys are never
+    loaded."""
+    N, H, d = 3000, 2, 128
+    pattern = dict(block=128, sink=1, local=7)
+    q = _gen((1, N, H, d), torch.bfloat16, 8)
+    k = _gen((1, N, H, d), torch.bfloat16, 9)
+    v = _gen((1, N, H, d), torch.bfloat16, 10)
+    ref = ssa.prefill(q, k, v, **pattern)
+    rows = np.arange(2048, 2304)
+    bad = torch.from_numpy(~_attended_union(rows, N, 128, 1, 7)).to(DEV)
     k2, v2 = k.clone(), v.clone()
     k2[:, bad] = float("nan")
     v2[:, bad] = float("nan")
