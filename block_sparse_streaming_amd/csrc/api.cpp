@@ -69,6 +69,12 @@ bool make_plan(ssa_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv
         split = kSsaSplitTokens;
     }
     split = (split + chunk - 1) / chunk * chunk;
+    if (plan->kind == ssa::kDecodeLatent) {
+        // Keep (split - 2) / page_size + 4 page ids within the kernel's table.
+        const int64_t cap = ((int64_t)(ssa::kDecodeLatentMaxPages - 4) * page_size + 1) / chunk * chunk;
+        if (cap < chunk) return false;
+        split = split < cap ? split : cap;
+    }
     if (split > kInt32Max) return false;
     const int64_t splits = (max_tokens + split - 1) / split;
     if (splits < 1 || splits > 65535) return false;

@@ -26,8 +26,9 @@
 //    split is a 64x576x(tokens) and a 64x(tokens)x512 product, so it runs on
 //    v_mfma_f32_16x16x32_bf16: S^T = K q^T (one 16-head column block per wave),
 //    then O^T = V^T P^T with P taken straight from the score registers. Chunks
-//    of 32 tokens are staged in LDS twice: row-major (for S) and transposed (for
-//    P.V), the next chunk's global loads in flight during the current chunk.
+//    of 32 latent rows stream global -> LDS through a 4-deep ring (a whole
+//    128-token split is requested at once); each row is stored once and the
+//    V^T operand is gathered from it with transpose reads.
 #include <type_traits>
 
 #include "common.h"
@@ -224,20 +225,30 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
 // ---------------------------------------------------------------------------
 constexpr int kLatDqk = 576;
 constexpr int kLatDv = 512;
-constexpr int kLatCh = 32;                  // tokens per LDS chunk
-constexpr int kKnStr = kLatDqk + 8;         // row-major K chunk, padded
-constexpr int kVtStr = kLatCh + 8;          // transposed V chunk, padded
+constexpr int kLatCh = 32;                          // tokens per LDS chunk
+constexpr int kLatUnits = kLatDqk / 8;              // 16-byte units per row
 constexpr int kLatThreads = 256;
+constexpr int kLatStages = 4;                       // ring depth
+constexpr int kLatDma = kLatCh * kLatUnits / 64 / 4;  // transfers per wave per chunk
+constexpr int kLatMaxPages = kDecodeLatentMaxPages;  // page ids of one split kept in LDS
+constexpr float kLatSlack = 8.f;                    // lazy-rescale slack (log2 units)
 
-// Position of token quad `quad` (tokens 4quad..4quad+3 of a 32-token chunk) in a
-// V^T row. In the 16x16 accumulator a lane of row group kg holds tokens
-// 4kg..4kg+3 of each 16-token block; the P.V B operand feeds those 8 tokens as
-// one 8-wide slot, so they are stored adjacently: pos = 8*kg + 4*block.
-__device__ __forceinline__ int lat_quad_pos(int quad) { return 8 * (quad & 3) + 4 * (quad >> 2); }
+// XOR swizzle of the 16-byte units of latent row r (1152 B = 128 mod 256):
+// the 16 rows read at one unit by a score-operand read, and the 8 rows x 2
+// units read by a half-wave's transpose read, both land in 16 bank groups.
+__device__ __forceinline__ int lat_swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
 
+// One work-group computes one split (up to split_tokens attended tokens of
+// one sequence) for up to 64 query heads of one kv head; wave w owns heads
+// 16w..16w+15. The split's latent rows arrive in 32-token chunks through an
+// LDS ring; S^T = K q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16, the
+// V^T operand gathered from the same row-major chunk by transpose reads.
 __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t kn[kLatCh * kKnStr];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[kLatDv * kVtStr];
+    __shared__ __attribute__((aligned(1024))) uint16_t c_b0[kLatCh * kLatDqk];
+    __shared__ __attribute__((aligned(1024))) uint16_t c_b1[kLatCh * kLatDqk];
+    __shared__ __attribute__((aligned(1024))) uint16_t c_b2[kLatCh * kLatDqk];
+    __shared__ __attribute__((aligned(1024))) uint16_t c_b3[kLatCh * kLatDqk];
+    __shared__ int32_t pids[kLatMaxPages];
 
     const int split = blockIdx.x;
     const int hc = blockIdx.y % a.plan.head_chunks, g = blockIdx.y / a.plan.head_chunks;
@@ -252,8 +263,51 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     if (p_begin >= sel.total) return;
     const int64_t p_end = p_begin + a.plan.split_tokens < sel.total ? p_begin + a.plan.split_tokens
                                                                       : sel.total;
-    const int64_t ntok = p_end - p_begin;
-    const int nch = (int)((ntok + kLatCh - 1) / kLatCh);
+    const int ntok = (int)(p_end - p_begin);
+    const int nch = (ntok + kLatCh - 1) / kLatCh;
+
+    // Page ids of the split: positions [p_begin, p_end) map to at most two
+    // token runs (one per attended range), each a run of logical pages.
+    const int P = a.page_size;
+    const int64_t e1 = p_end < sel.r1_end ? p_end : sel.r1_end;           // part in range 1: [p_begin, e1)
+    const int64_t s2 = p_begin > sel.r1_end ? p_begin : sel.r1_end;       // part in range 2: [s2, p_end)
+    const int64_t lp1 = p_begin / P;
+    const int n1 = e1 > p_begin ? (int)((e1 - 1) / P - lp1 + 1) : 0;
+    const int64_t t2 = sel.r2_begin + (s2 - sel.r1_end);                  // first token of part 2
+    const int64_t lp2 = t2 / P;
+    const int n2 = p_end > s2 ? (int)((sel.r2_begin + (p_end - sel.r1_end) - 1) / P - lp2 + 1) : 0;
+    for (int t = tid; t < n1 + n2; t += kLatThreads)
+        pids[t] = a.page_table[(int64_t)bb * a.max_pages + (t < n1 ? lp1 + t : lp2 + (t - n1))];
+    __syncthreads();
+
+    const uint16_t *kc = (const uint16_t *)a.kc + g * a.ks[2];
+    // Element offset of the latent row at split position pp (clamped to the
+    // split), relative to kc.
+    // Positions and tokens fit in 32 bits (context lengths are int32).
+    const uint32_t up_end = (uint32_t)p_end, ur1 = (uint32_t)sel.r1_end, ur2 = (uint32_t)sel.r2_begin;
+    const uint32_t uP = (uint32_t)P, ulp1 = (uint32_t)lp1, ulp2 = (uint32_t)lp2;
+    auto row_off = [&](uint32_t pp) __attribute__((always_inline)) -> int64_t {
+        pp = pp < up_end ? pp : up_end - 1;
+        const uint32_t tok = pp < ur1 ? pp : ur2 + (pp - ur1);
+        const uint32_t lp = tok / uP;
+        const int idx = pp < ur1 ? (int)(lp - ulp1) : n1 + (int)(lp - ulp2);
+        return (int64_t)pids[idx] * a.ks[0] + (int64_t)(tok - lp * uP) * a.ks[1];
+    };
+    // Transfers of chunk c: lane slot p of transfer n is chunk row p / 72 at
+    // physical unit p % 72, holding logical unit (p % 72) ^ lat_swz(row).
+    // Chunks past the last issue the same number of transfers (of row 0).
+    auto issue = [&](int c, uint16_t *buf) __attribute__((always_inline)) {
+        const bool real = c < nch;
+#pragma unroll
+        for (int n = 0; n < kLatDma; ++n) {
+            const int p = (wave * kLatDma + n) * 64 + lane;
+            const int r = p / kLatUnits;
+            const int unit = (p % kLatUnits) ^ lat_swz(r);
+            const int64_t off = real ? row_off((uint32_t)p_begin + (uint32_t)(c * kLatCh + r)) + unit * 8
+                                     : row_off((uint32_t)p_begin);
+            dma16(kc + off, buf + (wave * kLatDma + n) * 512);
+        }
+    };
 
     const int heads_here = a.group - hc * 64 < 64 ? a.group - hc * 64 : 64;
     const bool active = wave * 16 < heads_here;
@@ -271,109 +325,127 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
         }
     }
 
-    const uint16_t *kc = (const uint16_t *)a.kc + g * a.ks[2];
-    // Staging registers for one chunk: two (token quad, 16-byte column) units of
-    // the first 512 dims and one 16-byte column of the last 64 dims.
-    u32x4 pre[9];
-    auto fetch = [&](int c) {
-        const int64_t base = p_begin + (int64_t)c * kLatCh;
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-            const int u = tid + kLatThreads * t2;
-            const int dc = u & 63, quad = u >> 6;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int64_t pp = base + 4 * quad + rr;
-                pre[4 * t2 + rr] = u32x4{0u, 0u, 0u, 0u};
-                if (pp < p_end)
-                    pre[4 * t2 + rr] = *(const u32x4 *)(kc + token_row(a, bb, sel_token(sel, pp), a.ks) + dc * 8);
-            }
-        }
-        const int64_t pp = base + (tid >> 3);
-        pre[8] = u32x4{0u, 0u, 0u, 0u};
-        if (pp < p_end)
-            pre[8] = *(const u32x4 *)(kc + token_row(a, bb, sel_token(sel, pp), a.ks) + (64 + (tid & 7)) * 8);
-    };
-    auto stash = [&]() {
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-            const int u = tid + kLatThreads * t2;
-            const int dc = u & 63, quad = u >> 6;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) *(u32x4 *)(kn + (4 * quad + rr) * kKnStr + dc * 8) = pre[4 * t2 + rr];
-            const int pos = lat_quad_pos(quad);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                u32x2 w2 = {pick_pair(pre[4 * t2 + 0], pre[4 * t2 + 1], e),
-                            pick_pair(pre[4 * t2 + 2], pre[4 * t2 + 3], e)};
-                *(u32x2 *)(vt + (dc * 8 + e) * kVtStr + pos) = w2;
-            }
-        }
-        *(u32x4 *)(kn + (tid >> 3) * kKnStr + (64 + (tid & 7)) * 8) = pre[8];
-    };
-
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 oacc[kLatDv / 16];
 #pragma unroll
     for (int d = 0; d < kLatDv / 16; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    fetch(0);
-    for (int c = 0; c < nch; ++c) {
-        __syncthreads();
-        stash();
-        __syncthreads();
-        if (c + 1 < nch) fetch(c + 1);
-        if (!active) continue;
+    // Lane-constant LDS byte offsets.
+    // Score operand: row tb*16 + l16, unit 4ks + kg, swizzled by lat_swz(l16)
+    // (the tb*16 offset does not change the swizzle): two variants by ks parity.
+    const int ksw = lat_swz(l16);
+    const uint32_t k_lane = (uint32_t)l16 * (kLatDqk * 2);
+    const uint32_t k_even = (uint32_t)((kg ^ ksw) << 4), k_odd = (uint32_t)(((4 + kg) ^ ksw) << 4);
+    // Transpose reads: lane s of group kg reads token 16h + 4kg + s/4 at value
+    // column 16d + 4(s%4); its swizzle depends only on the lane.
+    const int tr_tok = 4 * kg + (l16 >> 2);
+    const int vsw = lat_swz(tr_tok);
+    const int uo = (l16 & 3) >> 1;
+    uint32_t v_lane[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+        v_lane[q4] = (uint32_t)tr_tok * (kLatDqk * 2) + (uint32_t)(((2 * q4 + uo) ^ vsw) << 4) + 8u * (l16 & 1);
 
+    auto compute = [&](int c, const uint16_t *buf) __attribute__((always_inline)) {
+        uint32_t kl = k_lane, ke = k_even, ko = k_odd;
+        asm volatile("" : "+v"(kl), "+v"(ke), "+v"(ko));
+        const char *cb = (const char *)buf;
         // S^T = K q^T: element r of block tb is token tb*16 + 4*kg + r, head l16.
         f32x4 sacc[2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             sacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint16_t *krow = kn + (tb * 16 + l16) * kKnStr + 8 * kg;
+            const char *rowp = cb + kl + tb * 16 * (kLatDqk * 2);
 #pragma unroll
             for (int ks = 0; ks < kLatDqk / 32; ++ks) {
-                const bf16x8 kf = *(const bf16x8 *)(krow + ks * 32);
+                const bf16x8 kf = *(const bf16x8 *)(rowp + 128 * (ks >> 1) + ((ks & 1) ? ko : ke));
                 sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[tb], 0, 0, 0);
             }
         }
-        const int64_t nvalid = ntok - (int64_t)c * kLatCh;
+        // Online softmax over this chunk (tokens past the split are masked),
+        // lazy rescale as in prefill.
+        const int nvalid = ntok - c * kLatCh;
         float mx = -INFINITY;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tk = tb * 16 + 4 * kg + r;
-                const float x = tk < nvalid ? sacc[tb][r] * a.scale_log2 : -INFINITY;
+                const float x = tk < nvalid ? sacc[tb][r] : -INFINITY;
                 sacc[tb][r] = x;
                 mx = fmaxf(mx, x);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLatSlack)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+            l_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < kLatDv / 16; ++d) oacc[d] *= alpha;
+            m_run = m_new;
+        }
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
         float p[8];
         float rs = 0.f;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[4 * tb + r] = fast_exp2(sacc[tb][r] - m_use);
+                p[4 * tb + r] = fast_exp2(__builtin_fmaf(sacc[tb][r], a.scale_log2, neg_m));
                 rs += p[4 * tb + r];
             }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
+        l_run += rs;
         const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                           pack_bf16x2(p[6], p[7])};
         const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+        // O^T += V^T P^T; slot e of lane (head l16, kg) is token 16(e/4) + 4kg + e%4.
+        uint32_t vl[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            vl[q4] = v_lane[q4];
+            asm volatile("" : "+v"(vl[q4]));
+        }
 #pragma unroll
         for (int d = 0; d < kLatDv / 16; ++d) {
-            oacc[d] *= alpha;
-            const bf16x8 vf = *(const bf16x8 *)(vt + (d * 16 + l16) * kVtStr + 8 * kg);
+            const char *vp = cb + vl[d & 3] + 128 * (d >> 2);
+            const i16x4 lo = lds_read_tr16(vp);
+            const i16x4 up = lds_read_tr16(vp + 16 * (kLatDqk * 2));
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
             oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[d], 0, 0, 0);
         }
+    };
+
+    // Ring pipeline (one barrier per chunk), as in prefill: wait for this
+    // wave's transfers of chunk c; the barrier publishes it and proves every
+    // wave is done with chunk c-1, whose buffer is refilled with c+S-1.
+    auto cbuf = [&](auto k) __attribute__((always_inline)) -> uint16_t * {
+        constexpr int b = decltype(k)::value % kLatStages;
+        if constexpr (b == 0) return c_b0;
+        else if constexpr (b == 1) return c_b1;
+        else if constexpr (b == 2) return c_b2;
+        else return c_b3;
+    };
+    auto step = [&](int c, auto k) __attribute__((always_inline)) {
+        constexpr int b = decltype(k)::value;
+        wait_vmcnt<(kLatStages - 2) * kLatDma>();
+        barrier_lds_drained();
+        issue(c + kLatStages - 1, cbuf(std::integral_constant<int, b + kLatStages - 1>{}));
+        if (active) compute(c, cbuf(k));
+    };
+    issue(0, c_b0);
+    issue(1, c_b1);
+    issue(2, c_b2);
+    for (int c = 0; c < nch; c += kLatStages) {
+        step(c, std::integral_constant<int, 0>{});
+        if (c + 1 >= nch) break;
+        step(c + 1, std::integral_constant<int, 1>{});
+        if (c + 2 >= nch) break;
+        step(c + 2, std::integral_constant<int, 2>{});
+        if (c + 3 >= nch) break;
+        step(c + 3, std::integral_constant<int, 3>{});
     }
+    wait_vmcnt<0>();
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);

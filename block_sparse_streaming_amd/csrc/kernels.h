@@ -23,6 +23,11 @@ hipError_t launch_prefill(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hi
 
 enum DecodeKind { kDecodeValu = 0, kDecodeLatent = 1 };
 
+// The latent kernel keeps the page ids of one split in LDS. A split of T
+// positions covers at most two token runs, so at most (T - 2) / page_size + 4
+// pages; the planner keeps that within this bound.
+constexpr int kDecodeLatentMaxPages = 256;
+
 // How a decode call is cut into work-groups. Computed on the host from shapes
 // only (context lengths live on the device), so the workspace size is known
 // before the call.

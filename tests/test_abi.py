@@ -115,5 +115,10 @@ def test_workspace_sizes():
     assert ws(torch.bfloat16, 1, 16, 16, 128, 128, 128, 2) == -(-16 * 2 * 128 * 4 // 256) * 256 + 16 * 2 * 4
     # full decode grows with the context
     assert ws(torch.bfloat16, 32, 64, 1, 576, 512, 128, 1024, full=True) > need
+    # latent full decode with 2-token pages: the split is capped at 480 tokens
+    # (at most (480 - 2) // 2 + 4 = 243 pages), so 262144 tokens need 547 splits
+    slots = 4 * 64 * 547
+    assert ws(torch.bfloat16, 4, 64, 1, 576, 512, 2, 131072, full=True) == \
+        -(-slots * 512 * 4 // 256) * 256 + slots * 4
     assert ws(torch.bfloat16, 1, 4, 3, 128, 128, 128, 8) == 0          # invalid heads
     assert ws(torch.bfloat16, 1, 4, 4, 128, 128, 128, 8, local=0) == 0

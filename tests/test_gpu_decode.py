@@ -97,6 +97,22 @@ def test_latent_two_kv_heads():
     _check(cfg, inp, PAT, what="latent 2 kv heads")
 
 
+@pytest.mark.parametrize("page_size", [1, 2])
+def test_latent_tiny_pages_wide_table(page_size):
+    """Pages of 1-2 tokens under a page table 131072 columns wide: the full
+    decode plan's split is then bounded by how many page ids one work-group
+    keeps (the split would otherwise cover more than 256 pages)."""
+    cfg = _cfg(torch.bfloat16, 64, 1, 576, 512, latent=True, seed=27 + page_size)
+    lens = (3000, 1, 2500, 4097)
+    inp = inputs.decode_inputs(cfg, DEV, lens=lens, page_size=page_size)
+    wide = np.zeros((len(lens), 131072), np.int32)
+    wide[:, :inp.table_np.shape[1]] = inp.table_np
+    inp = inputs.DecodeInputs(inp.q, inp.k_cache, inp.v_cache, torch.from_numpy(wide).to(DEV),
+                              inp.ctx_lens, wide, lens)
+    _check(cfg, inp, PAT, what=f"latent P{page_size}", page_size=page_size)
+    _check(cfg, inp, PAT, full=True, what=f"latent P{page_size} full", page_size=page_size)
+
+
 def test_config3_latent_full_size():
     """32 sequences x 131072 tokens, shuffled pages: SSA decode on every
     sequence, full decode on two of them (the oracle's cost is the limit)."""
