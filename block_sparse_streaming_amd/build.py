@@ -18,6 +18,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssa.so")
 SOURCES = ["api.cpp", "prefill.hip", "decode.hip"]
 ARCH = "gfx950"
+# decode.hip's only MFMA kernel keeps its output accumulators in VGPRs (their
+# rescale is VALU work) and its read-only q operand in AGPRs; the VGPR form of
+# MFMA lets the compiler do that without copying the accumulators each chunk.
+EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -43,7 +47,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [cc, *common_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *common_flags(), *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -83,6 +83,32 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_wave_base) {
     __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_wave_base, 16, 0, 0);
 }
 
+// The same 16-byte global -> LDS transfer, issued from inline assembly so that
+// the compiler does not track it: it then adds no waits of its own before LDS
+// reads (its alias tracking of these transfers does not survive loops), and
+// the caller alone orders the buffer with wait_vmcnt + a barrier. The
+// instruction writes no VGPR. lds_wave_base is the wave-uniform LDS byte
+// address of lane 0's 16 bytes.
+// M0 carries the LDS address; the statement restores it, since the compiler
+// reserves M0 and assumes it unchanged.
+__device__ __forceinline__ void dma16_untracked(const void *src, uint32_t lds_wave_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds_wave_base)
+        : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const lds_void *)p;
+}
+
 // LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // result lane i, element k is element (i % 4) of the 8 bytes addressed by
 // lane 4k + i/4. If lane s of a group points at row s/4, columns 4(s%4)..+3 of

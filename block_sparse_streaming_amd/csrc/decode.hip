@@ -225,13 +225,15 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
 // ---------------------------------------------------------------------------
 constexpr int kLatDqk = 576;
 constexpr int kLatDv = 512;
-constexpr int kLatCh = 32;                          // tokens per LDS chunk
-constexpr int kLatUnits = kLatDqk / 8;              // 16-byte units per row
+constexpr int kLatCh = 32;                            // latent rows per LDS buffer
+constexpr int kLatUnits = kLatDqk / 8;                // 16-byte units per row
 constexpr int kLatThreads = 256;
-constexpr int kLatStages = 4;                       // ring depth
-constexpr int kLatDma = kLatCh * kLatUnits / 64 / 4;  // transfers per wave per chunk
-constexpr int kLatMaxPages = kDecodeLatentMaxPages;  // page ids of one split kept in LDS
-constexpr float kLatSlack = 8.f;                    // lazy-rescale slack (log2 units)
+constexpr int kLatBufs = 4;                           // ring depth
+constexpr int kLatRowsPerWave = kLatCh / 4;           // rows each wave transfers per chunk
+constexpr int kLatDma = kLatRowsPerWave * kLatUnits / 64;  // transfers per wave per chunk
+constexpr int kLatMaxPages = kDecodeLatentMaxPages;   // page ids of one split kept in LDS
+constexpr float kLatSlack = 8.f;                      // lazy-rescale slack (log2 units)
+static_assert(kLatDma * 64 == kLatRowsPerWave * kLatUnits, "a wave moves whole rows");
 
 // XOR swizzle of the 16-byte units of latent row r (1152 B = 128 mod 256):
 // the 16 rows read at one unit by a score-operand read, and the 8 rows x 2
@@ -240,20 +242,26 @@ __device__ __forceinline__ int lat_swz(int r) { return (((r >> 1) & 3) << 1) | (
 
 // One work-group computes one split (up to split_tokens attended tokens of
 // one sequence) for up to 64 query heads of one kv head; wave w owns heads
-// 16w..16w+15. The split's latent rows arrive in 32-token chunks through an
-// LDS ring; S^T = K q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16, the
-// V^T operand gathered from the same row-major chunk by transpose reads.
+// 16w..16w+15. The split's latent rows arrive in 32-token chunks through a
+// ring of four LDS buffers (an SSA split of 128 tokens is requested at once).
+// Per chunk: S^T = K q^T, an online softmax with lazy rescaling, and
+// O^T += V^T P^T with P taken straight from the score registers; both
+// products run on v_mfma_f32_16x16x32_bf16 and the V^T operand is gathered
+// from the row-major buffer by transpose reads. q stays in AGPRs (it is only
+// an MFMA source) so the VGPRs hold the output accumulators.
 __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const DecodeArgs a) {
     __shared__ __attribute__((aligned(1024))) uint16_t c_b0[kLatCh * kLatDqk];
     __shared__ __attribute__((aligned(1024))) uint16_t c_b1[kLatCh * kLatDqk];
     __shared__ __attribute__((aligned(1024))) uint16_t c_b2[kLatCh * kLatDqk];
     __shared__ __attribute__((aligned(1024))) uint16_t c_b3[kLatCh * kLatDqk];
     __shared__ int32_t pids[kLatMaxPages];
+    __shared__ int64_t rowtab[4][kLatRowsPerWave];
 
     const int split = blockIdx.x;
     const int hc = blockIdx.y % a.plan.head_chunks, g = blockIdx.y / a.plan.head_chunks;
     const int bb = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, kg = lane >> 4;
 
     const int64_t L = a.ctx_lens[bb];
@@ -278,42 +286,13 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     const int n2 = p_end > s2 ? (int)((sel.r2_begin + (p_end - sel.r1_end) - 1) / P - lp2 + 1) : 0;
     for (int t = tid; t < n1 + n2; t += kLatThreads)
         pids[t] = a.page_table[(int64_t)bb * a.max_pages + (t < n1 ? lp1 + t : lp2 + (t - n1))];
-    __syncthreads();
-
-    const uint16_t *kc = (const uint16_t *)a.kc + g * a.ks[2];
-    // Element offset of the latent row at split position pp (clamped to the
-    // split), relative to kc.
-    // Positions and tokens fit in 32 bits (context lengths are int32).
-    const uint32_t up_end = (uint32_t)p_end, ur1 = (uint32_t)sel.r1_end, ur2 = (uint32_t)sel.r2_begin;
-    const uint32_t uP = (uint32_t)P, ulp1 = (uint32_t)lp1, ulp2 = (uint32_t)lp2;
-    auto row_off = [&](uint32_t pp) __attribute__((always_inline)) -> int64_t {
-        pp = pp < up_end ? pp : up_end - 1;
-        const uint32_t tok = pp < ur1 ? pp : ur2 + (pp - ur1);
-        const uint32_t lp = tok / uP;
-        const int idx = pp < ur1 ? (int)(lp - ulp1) : n1 + (int)(lp - ulp2);
-        return (int64_t)pids[idx] * a.ks[0] + (int64_t)(tok - lp * uP) * a.ks[1];
-    };
-    // Transfers of chunk c: lane slot p of transfer n is chunk row p / 72 at
-    // physical unit p % 72, holding logical unit (p % 72) ^ lat_swz(row).
-    // Chunks past the last issue the same number of transfers (of row 0).
-    auto issue = [&](int c, uint16_t *buf) __attribute__((always_inline)) {
-        const bool real = c < nch;
-#pragma unroll
-        for (int n = 0; n < kLatDma; ++n) {
-            const int p = (wave * kLatDma + n) * 64 + lane;
-            const int r = p / kLatUnits;
-            const int unit = (p % kLatUnits) ^ lat_swz(r);
-            const int64_t off = real ? row_off((uint32_t)p_begin + (uint32_t)(c * kLatCh + r)) + unit * 8
-                                     : row_off((uint32_t)p_begin);
-            dma16(kc + off, buf + (wave * kLatDma + n) * 512);
-        }
-    };
 
     const int heads_here = a.group - hc * 64 < 64 ? a.group - hc * 64 : 64;
     const bool active = wave * 16 < heads_here;
     const int head = g * a.group + hc * 64 + wave * 16 + l16;  // this lane's query head
 
-    // q^T operand (16 heads x 576 per wave) in registers.
+    // q^T operand (16 heads x 576 per wave) in registers, loaded before any
+    // transfer so that the transfer waits below count transfers only.
     bf16x8 qf[kLatDqk / 32];
     {
         const uint16_t *qp = (const uint16_t *)a.q + ((int64_t)bb * a.Hq + head) * kLatDqk + 8 * kg;
@@ -323,12 +302,42 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
             if (active) w = *(const u32x4 *)(qp + ks * 32);
             qf[ks] = __builtin_bit_cast(bf16x8, w);
         }
-    }
-
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 oacc[kLatDv / 16];
+        // q is only ever an MFMA source operand, which may sit in AGPRs: park
+        // it there so the VGPRs hold the output accumulators and the scores.
 #pragma unroll
-    for (int d = 0; d < kLatDv / 16; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < kLatDqk / 32; ++ks) asm volatile("" : "+a"(qf[ks]));
+    }
+    __syncthreads();
+
+    const uint16_t *kc = (const uint16_t *)a.kc + g * a.ks[2];
+    // Element offset (relative to kc) of the latent row at split position pp,
+    // clamped to the split. Positions and tokens fit in 32 bits.
+    const uint32_t up_end = (uint32_t)p_end, ur1 = (uint32_t)sel.r1_end, ur2 = (uint32_t)sel.r2_begin;
+    const uint32_t uP = (uint32_t)P, ulp1 = (uint32_t)lp1, ulp2 = (uint32_t)lp2;
+    auto row_off = [&](uint32_t pp) __attribute__((always_inline)) -> int64_t {
+        pp = pp < up_end ? pp : up_end - 1;
+        const uint32_t tok = pp < ur1 ? pp : ur2 + (pp - ur1);
+        const uint32_t lp = tok / uP;
+        const int idx = pp < ur1 ? (int)(lp - ulp1) : n1 + (int)(lp - ulp2);
+        return (int64_t)pids[idx] * a.ks[0] + (int64_t)(tok - lp * uP) * a.ks[1];
+    };
+    // Transfers of chunk c: wave w moves rows 8w..8w+7. Lane slot p = 64n + lane
+    // of its transfer n is row 8w + p / 72 at physical unit p % 72, which holds
+    // logical unit (p % 72) ^ lat_swz(row). The wave's eight row offsets are
+    // computed once by lanes 0..7 into rowtab (rows past the split's end
+    // repeat its last row).
+    auto issue = [&](int c, uint16_t *buf) __attribute__((always_inline)) {
+        if (lane < kLatRowsPerWave) {
+            rowtab[wave][lane] = row_off((uint32_t)p_begin + (uint32_t)(c * kLatCh + wave * kLatRowsPerWave + lane));
+        }
+#pragma unroll
+        for (int n = 0; n < kLatDma; ++n) {
+            const int p = n * 64 + lane;
+            const int r = p / kLatUnits;
+            const int unit = (p % kLatUnits) ^ lat_swz(wave * kLatRowsPerWave + r);
+            dma16_untracked(kc + rowtab[wave][r] + unit * 8, lds_addr(buf + (wave * kLatDma + n) * 512));
+        }
+    };
 
     // Lane-constant LDS byte offsets.
     // Score operand: row tb*16 + l16, unit 4ks + kg, swizzled by lat_swz(l16)
@@ -346,66 +355,73 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     for (int q4 = 0; q4 < 4; ++q4)
         v_lane[q4] = (uint32_t)tr_tok * (kLatDqk * 2) + (uint32_t)(((2 * q4 + uo) ^ vsw) << 4) + 8u * (l16 & 1);
 
-    auto compute = [&](int c, const uint16_t *buf) __attribute__((always_inline)) {
+    // S^T of chunk c from `buf`: element r of s[tb] is token tb*16 + 4kg + r of
+    // the chunk (for head l16), -inf past the split's end.
+    auto scores = [&](const uint16_t *buf, int c, f32x4 (&s)[2]) __attribute__((always_inline)) {
         uint32_t kl = k_lane, ke = k_even, ko = k_odd;
         asm volatile("" : "+v"(kl), "+v"(ke), "+v"(ko));
-        const char *cb = (const char *)buf;
-        // S^T = K q^T: element r of block tb is token tb*16 + 4*kg + r, head l16.
-        f32x4 sacc[2];
+        const char *rowp = (const char *)buf + kl;
+        s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            sacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const char *rowp = cb + kl + tb * 16 * (kLatDqk * 2);
+        for (int ks = 0; ks < kLatDqk / 32; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < kLatDqk / 32; ++ks) {
-                const bf16x8 kf = *(const bf16x8 *)(rowp + 128 * (ks >> 1) + ((ks & 1) ? ko : ke));
-                sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[tb], 0, 0, 0);
+            for (int tb = 0; tb < 2; ++tb) {
+                const bf16x8 kf = *(const bf16x8 *)(rowp + tb * 16 * (kLatDqk * 2) + 128 * (ks >> 1) +
+                                                    ((ks & 1) ? ko : ke));
+                s[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[tb], 0, 0, 0);
             }
-        }
-        // Online softmax over this chunk (tokens past the split are masked),
-        // lazy rescale as in prefill.
         const int nvalid = ntok - c * kLatCh;
-        float mx = -INFINITY;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tk = tb * 16 + 4 * kg + r;
-                const float x = tk < nvalid ? sacc[tb][r] : -INFINITY;
-                sacc[tb][r] = x;
-                mx = fmaxf(mx, x);
-            }
+            for (int r = 0; r < 4; ++r)
+                if (tb * 16 + 4 * kg + r >= nvalid) s[tb][r] = -INFINITY;
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 oacc[kLatDv / 16];
+#pragma unroll
+    for (int d = 0; d < kLatDv / 16; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // One chunk: scores, online softmax (lazy rescale), then O^T += V^T P^T.
+    // Slot e of lane (head l16, kg) in the P^T operand is token
+    // 16(e/4) + 4kg + e%4 of the chunk.
+    auto compute = [&](const uint16_t *buf, int c) __attribute__((always_inline)) {
+        f32x4 s[2];
+        scores(buf, c, s);
+        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kLatSlack)) {
             const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+            const float alpha = fast_exp2(m_run - m_new);  // 0 on the first chunk
             l_run *= alpha;
 #pragma unroll
             for (int d = 0; d < kLatDv / 16; ++d) oacc[d] *= alpha;
             m_run = m_new;
         }
-        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
         float p[8];
         float rs = 0.f;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[4 * tb + r] = fast_exp2(__builtin_fmaf(sacc[tb][r], a.scale_log2, neg_m));
+                p[4 * tb + r] = fast_exp2(__builtin_fmaf(s[tb][r], a.scale_log2, -m_run));
                 rs += p[4 * tb + r];
             }
         l_run += rs;
         const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                           pack_bf16x2(p[6], p[7])};
         const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-        // O^T += V^T P^T; slot e of lane (head l16, kg) is token 16(e/4) + 4kg + e%4.
         uint32_t vl[4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             vl[q4] = v_lane[q4];
             asm volatile("" : "+v"(vl[q4]));
         }
+        const char *cb = (const char *)buf;
 #pragma unroll
         for (int d = 0; d < kLatDv / 16; ++d) {
             const char *vp = cb + vl[d & 3] + 128 * (d >> 2);
@@ -416,11 +432,12 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
         }
     };
 
-    // Ring pipeline (one barrier per chunk), as in prefill: wait for this
-    // wave's transfers of chunk c; the barrier publishes it and proves every
-    // wave is done with chunk c-1, whose buffer is refilled with c+S-1.
+    // Ring of four buffers, one barrier per chunk: wait for this wave's share
+    // of chunk c (the transfers still allowed in flight are those of chunks
+    // c+1 and c+2, when they exist); the barrier publishes chunk c and proves
+    // every wave is done with chunk c-1, whose buffer then takes chunk c+3.
     auto cbuf = [&](auto k) __attribute__((always_inline)) -> uint16_t * {
-        constexpr int b = decltype(k)::value % kLatStages;
+        constexpr int b = decltype(k)::value % kLatBufs;
         if constexpr (b == 0) return c_b0;
         else if constexpr (b == 1) return c_b1;
         else if constexpr (b == 2) return c_b2;
@@ -428,15 +445,17 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     };
     auto step = [&](int c, auto k) __attribute__((always_inline)) {
         constexpr int b = decltype(k)::value;
-        wait_vmcnt<(kLatStages - 2) * kLatDma>();
+        if (c + 2 < nch) wait_vmcnt<2 * kLatDma>();
+        else if (c + 1 < nch) wait_vmcnt<kLatDma>();
+        else wait_vmcnt<0>();
         barrier_lds_drained();
-        issue(c + kLatStages - 1, cbuf(std::integral_constant<int, b + kLatStages - 1>{}));
-        if (active) compute(c, cbuf(k));
+        if (c + 3 < nch) issue(c + 3, cbuf(std::integral_constant<int, b + 3>{}));
+        if (active) compute(cbuf(k), c);
     };
     issue(0, c_b0);
-    issue(1, c_b1);
-    issue(2, c_b2);
-    for (int c = 0; c < nch; c += kLatStages) {
+    if (1 < nch) issue(1, c_b1);
+    if (2 < nch) issue(2, c_b2);
+    for (int c = 0; c < nch; c += kLatBufs) {
         step(c, std::integral_constant<int, 0>{});
         if (c + 1 >= nch) break;
         step(c + 1, std::integral_constant<int, 1>{});
@@ -445,7 +464,6 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
         if (c + 3 >= nch) break;
         step(c + 3, std::integral_constant<int, 3>{});
     }
-    wait_vmcnt<0>();
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
@@ -459,43 +477,94 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the splits of one (sequence, query head).
+// Merge of the splits of one (sequence, query head): one wave each.
 // ---------------------------------------------------------------------------
-template <bool kBF16>
-__global__ __launch_bounds__(256) void decode_merge(const DecodeArgs a, int D) {
+constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 8;  // splits whose partial outputs are loaded together
+
+// Lane i owns output elements E*i .. E*i + E - 1 (E = D / 64). The split
+// weights exp2(lse_s - M) / Z are computed once per split by lane s % 64 and
+// broadcast with readlane.
+template <bool kBF16, int D>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a) {
     using Elem = std::conditional_t<kBF16, uint16_t, float>;
-    const int h = blockIdx.x, bb = blockIdx.y, tid = threadIdx.x;
+    constexpr int E = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * (kMergeThreads / 64) + (threadIdx.x >> 6);  // bb * Hq + h
+    if (row >= a.B * a.Hq) return;
+    const int bb = row / a.Hq;
     const int64_t L = a.ctx_lens[bb];
-    Elem *out = (Elem *)a.o + ((int64_t)bb * a.Hq + h) * D;
+    Elem *out = (Elem *)a.o + (int64_t)row * D + E * lane;
     int ns = 0;
     if (L > 0) {
         const Sel sel = select_tokens(L, a);
         ns = (int)((sel.total + a.plan.split_tokens - 1) / a.plan.split_tokens);
     }
     if (ns == 0) {
-        for (int d = tid; d < D; d += blockDim.x) out[d] = Elem(0);
-        if (tid == 0 && a.lse) a.lse[(int64_t)bb * a.Hq + h] = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < E; ++e) out[e] = Elem(0);
+        if (lane == 0 && a.lse) a.lse[row] = -INFINITY;
         return;
     }
-    const int64_t slot0 = ((int64_t)bb * a.Hq + h) * a.plan.max_splits;
+    const int64_t slot0 = (int64_t)row * a.plan.max_splits;
     const float *wl = a.ws_lse + slot0;
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, wl[s]);
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, wl[s]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     float Z = 0.f;
-    for (int s = 0; s < ns; ++s) Z += fast_exp2(wl[s] - M);
+    for (int s = lane; s < ns; s += 64) Z += fast_exp2(wl[s] - M);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Z += __shfl_xor(Z, o);
     const float inv = 1.f / Z;
-    const float *wo = a.ws_o + slot0 * D;
-    for (int d = tid; d < D; d += blockDim.x) {
-        float o = 0.f;
-        for (int s = 0; s < ns; ++s) o += fast_exp2(wl[s] - M) * wo[(int64_t)s * D + d];
-        o *= inv;
-        if constexpr (kBF16) {
-            out[d] = (uint16_t)(pack_bf16x2(o, 0.f) & 0xffffu);
-        } else {
-            out[d] = o;
+
+    const float *wo = a.ws_o + slot0 * D + E * lane;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int s64 = 0; s64 < ns; s64 += 64) {
+        const float wlane = s64 + lane < ns ? fast_exp2(wl[s64 + lane] - M) * inv : 0.f;
+        const int nb = ns - s64 < 64 ? ns - s64 : 64;
+        for (int s0 = 0; s0 < nb; s0 += kMergeBatch) {
+            float part[kMergeBatch][E];
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const int s = s0 + u < nb ? s0 + u : nb - 1;
+                const float *src = wo + (int64_t)(s64 + s) * D;
+#pragma unroll
+                for (int e4 = 0; e4 < (E + 3) / 4; ++e4) {
+                    if constexpr (E >= 4) {
+                        const f32x4 v = *(const f32x4 *)(src + 4 * e4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) part[u][4 * e4 + e] = v[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) part[u][e] = src[e];
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const float wf = s0 + u < nb ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlane), s0 + u)) : 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(wf, part[u][e], acc[e]);
+            }
         }
     }
-    if (tid == 0 && a.lse) a.lse[(int64_t)bb * a.Hq + h] = (M + log2f(Z)) * kLn2;
+    if constexpr (kBF16) {
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+            if constexpr (E == 1) {
+                out[0] = (uint16_t)(pack_bf16x2(acc[0], 0.f) & 0xffffu);
+            } else {
+                *(uint32_t *)(out + e) = pack_bf16x2(acc[e], acc[e + 1]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) out[e] = acc[e];
+    }
+    if (lane == 0 && a.lse) a.lse[row] = (M + log2f(Z)) * kLn2;
 }
 
 template <bool kBF16, int D, int G>
@@ -553,10 +622,18 @@ hipError_t launch_decode(bool bf16, int d_qk, int d_v, const DecodeArgs &a, hipS
         err = bf16 ? launch_valu_d<true>(d_qk, a, stream) : launch_valu_d<false>(d_qk, a, stream);
     }
     if (err != hipSuccess) return err;
-    int D = d_v;
-    void *margs[] = {(void *)&a, (void *)&D};
-    return hipLaunchKernel(bf16 ? (const void *)decode_merge<true> : (const void *)decode_merge<false>,
-                           dim3(a.Hq, a.B), dim3(256), margs, 0, stream);
+    const void *merge;
+    switch (d_v) {
+        case 64: merge = bf16 ? (const void *)decode_merge<true, 64> : (const void *)decode_merge<false, 64>; break;
+        case 128: merge = bf16 ? (const void *)decode_merge<true, 128> : (const void *)decode_merge<false, 128>; break;
+        case 256: merge = bf16 ? (const void *)decode_merge<true, 256> : (const void *)decode_merge<false, 256>; break;
+        case 512: merge = bf16 ? (const void *)decode_merge<true, 512> : (const void *)decode_merge<false, 512>; break;
+        default: return hipErrorInvalidValue;
+    }
+    void *margs[] = {(void *)&a};
+    const int rows_per_wg = kMergeThreads / 64;
+    const int64_t wgs = ((int64_t)a.B * a.Hq + rows_per_wg - 1) / rows_per_wg;
+    return hipLaunchKernel(merge, dim3((unsigned)wgs), dim3(kMergeThreads), margs, 0, stream);
 }
 
 }  // namespace ssa
