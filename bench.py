@@ -4,18 +4,23 @@
 Headline (one JSON line on stdout): ssa_prefill throughput in TFLOP/s on the
 32K-token bf16 workload (B=1, N=32768, 16 heads, d=128, b=128, s=1, l=7),
 counted as algorithmic flops 2*(d_qk + d_v) per attended (query, key) pair.
-The same line carries the decode half of the metric (ssa_decode and
-full_attn_decode HBM GB/s on the 128K-context latent workload), the roofline
-of each kernel and the CPU oracle timed on a bounded sample of the prefill.
+The same line carries the other workloads of the metric: prefill at 2K (fp32)
+and 256K tokens, SSA and full-attention decode on the 128K-context latent
+workload and SSA decode on the ragged 4K-1M workload (HBM GB/s of algorithmic
+bytes), each against its roofline, and the CPU oracle timed on the prefill.
 
 Inputs are synthetic (seeded N(0,1)) and resident in HBM before timing.
-Timing uses HIP events on the stream the kernels run on.
+Timing uses HIP events recorded on the stream the kernels are launched on
+(torch's current stream, which the binding passes to the library).
+
+--profile {prefill,decode,copy} runs one short workload and prints nothing
+else, for rocprofv3 counter collection (copy: a plain 1 GiB device copy whose
+counter readings calibrate FETCH_SIZE / WRITE_SIZE).
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -28,6 +33,7 @@ if ROOT not in sys.path:
 
 METRIC = "SSA prefill TFLOP/s + decode HBM GB/s (b=128,s=1,l=7) at 32K–256K ctx"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 matrix / vector
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 
@@ -49,7 +55,8 @@ def decode_selected_tokens(L: int, block: int, sink: int, local: int) -> int:
 
 
 def time_events(fn, iters: int) -> float:
-    """Average milliseconds of fn() over iters back-to-back calls, by HIP events."""
+    """Average milliseconds of fn() over iters back-to-back calls, by HIP events
+    on the current stream, synchronised before and after."""
     import torch
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -61,36 +68,107 @@ def time_events(fn, iters: int) -> float:
     return start.elapsed_time(stop) / iters
 
 
-def bench_prefill(steps: int, warmup: int):
+def recorded_traffic(keys: list[str]):
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (copy-calibrated) and stored in profiles/traffic.json, summed over `keys`;
+    None when a kernel has no record or its sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    total = 0.0
+    for key in keys:
+        entry = data.get(key)
+        if entry is None:
+            return None
+        h = hashlib.sha256()
+        for name in entry["sources"]:
+            with open(os.path.join(ROOT, "block_sparse_streaming_amd", "csrc", name), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != entry["source_sha256"]:
+            return None
+        total += entry["bytes_per_launch"]
+    return total
+
+
+def free_gpu():
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Prefill
+# ---------------------------------------------------------------------------
+def prefill_setup(cfg_id: int):
     import torch
     import block_sparse_streaming_amd as ssa
     from block_sparse_streaming_amd import inputs
 
-    cfg = inputs.CONFIGS[2]
-    pat = inputs.PATTERN
+    cfg = inputs.CONFIGS[cfg_id]
     q, k, v = inputs.prefill_inputs(cfg, "cuda:0")
     out = torch.empty((cfg.B, cfg.N, cfg.Hq, cfg.d_v), dtype=cfg.dtype, device="cuda:0")
 
     def step():
-        ssa.prefill(q, k, v, **pat, scale=cfg.scale, out=out)
+        ssa.prefill(q, k, v, **inputs.PATTERN, scale=cfg.scale, out=out)
 
+    return cfg, step
+
+
+def bench_prefill(cfg_id: int, steps: int, warmup: int):
+    import torch
+    from block_sparse_streaming_amd import inputs
+
+    cfg, step = prefill_setup(cfg_id)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     ms = time_events(step, steps)
-    wall = time.perf_counter() - t0
-    pairs = attended_pairs(cfg.N, **pat) * cfg.Hq * cfg.B
+    pairs = attended_pairs(cfg.N, **inputs.PATTERN) * cfg.Hq * cfg.B
     flops = pairs * 2 * (cfg.d_qk + cfg.d_v)
     tflops = flops / (ms * 1e-3) / 1e12
-    return cfg, ms, wall, flops, tflops
+    bf16 = cfg.dtype == torch.bfloat16
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+    kernel = (f"ssa_prefill_bf16<{cfg.d_qk}, {cfg.d_v}>" if bf16 else
+              f"ssa_prefill_f32<{cfg.d_qk}, {cfg.d_v}>")
+    grid = -(-cfg.N // 128) * cfg.Hq * cfg.B * 256
+    res = {"workload": cfg.name, "ms": ms, "steps": steps, "algorithmic_flops": flops,
+           "TFLOP/s": tflops,
+           "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                        "frac": tflops / peak,
+                        "traffic": recorded_traffic([f"{kernel} grid={grid}"])}}
+    del step
+    free_gpu()
+    return cfg, res
 
 
-def bench_decode(iters: int):
+# ---------------------------------------------------------------------------
+# Decode
+# ---------------------------------------------------------------------------
+def decode_bytes(cfg, lens, selected, page_size: int) -> int:
+    """Algorithmic bytes of one decode call: the attended cache rows (a value
+    that aliases the key row counts once), q, o, the page-table entries of the
+    attended pages and the context lengths."""
+    esz = 2
+    tok_bytes = cfg.Hkv * cfg.d_qk * esz if cfg.latent else cfg.Hkv * (cfg.d_qk + cfg.d_v) * esz
+    qo = len(lens) * cfg.Hq * (cfg.d_qk + cfg.d_v) * esz
+    return sum(selected) * tok_bytes + qo + sum(-(-t // page_size) for t in selected) * 4 + len(lens) * 4
+
+
+def decode_roofline(gbs: float, traffic_keys=None) -> dict:
+    return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS,
+            "traffic": recorded_traffic(traffic_keys) if traffic_keys else None}
+
+
+def bench_decode_latent(iters: int):
     """ssa_decode and full_attn_decode on the 128K latent workload. The SSA
-    call rotates over 8 page-table/query instances (8 x 42 MB > the 256 MB
-    Infinity Cache) and is replayed from a HIP graph so that host launch
-    overhead does not pad the 10-us kernels."""
+    call rotates over 8 page-table/query instances, whose selected pages
+    (8 x 42 MB) exceed the 256 MB Infinity Cache, and is replayed from a HIP
+    graph so that host launch overhead does not pad the short kernels."""
     import torch
     import block_sparse_streaming_amd as ssa
     from block_sparse_streaming_amd import inputs
@@ -108,12 +186,13 @@ def bench_decode(iters: int):
         insts.append((qr, torch.from_numpy(table).to(dev)))
     B, Hq, dv = cfg.B, cfg.Hq, cfg.d_v
     outs = [torch.empty((B, Hq, dv), dtype=cfg.dtype, device=dev) for _ in range(n_inst)]
+    max_pages = base.page_table.shape[1]
     ws_ssa = torch.empty(ssa.decode_workspace_size(cfg.dtype, B, Hq, cfg.Hkv, cfg.d_qk, dv,
-                                                   inputs.PAGE_SIZE, base.page_table.shape[1]),
+                                                   inputs.PAGE_SIZE, max_pages),
                          dtype=torch.uint8, device=dev)
     ws_full = torch.empty(ssa.decode_workspace_size(cfg.dtype, B, Hq, cfg.Hkv, cfg.d_qk, dv,
-                                                    inputs.PAGE_SIZE, base.page_table.shape[1],
-                                                    full=True), dtype=torch.uint8, device=dev)
+                                                    inputs.PAGE_SIZE, max_pages, full=True),
+                          dtype=torch.uint8, device=dev)
 
     def ssa_call(r):
         qr, tr = insts[r]
@@ -145,29 +224,65 @@ def bench_decode(iters: int):
     ssa_ms = time_events(graph.replay, n_graph) / (reps * n_inst)
     full_ms = time_events(full_call, max(3, iters // 16))
 
-    tok_bytes = cfg.d_qk * 2                          # latent row; the value aliases it
-    sel = sum(decode_selected_tokens(L, **pat) for L in base.lens)
-    sel_pages = sum(-(-decode_selected_tokens(L, **pat) // inputs.PAGE_SIZE) for L in base.lens)
-    qo = B * Hq * (cfg.d_qk + dv) * 2
-    ssa_bytes = sel * tok_bytes + qo + sel_pages * 4 + B * 4
-    full_tokens = sum(base.lens)
-    full_bytes = full_tokens * tok_bytes + qo + sum(-(-L // inputs.PAGE_SIZE) for L in base.lens) * 4 + B * 4
+    sel = [decode_selected_tokens(L, **pat) for L in base.lens]
+    ssa_bytes = decode_bytes(cfg, base.lens, sel, inputs.PAGE_SIZE)
+    full_bytes = decode_bytes(cfg, base.lens, list(base.lens), inputs.PAGE_SIZE)
     ssa_gbs = ssa_bytes / (ssa_ms * 1e-3) / 1e9
     full_gbs = full_bytes / (full_ms * 1e-3) / 1e9
-    return {
+    res = {
         "workload": cfg.name,
         "ssa_decode": {"us": ssa_ms * 1e3, "bytes": ssa_bytes, "GB/s": ssa_gbs,
-                       "roofline": {"bound": "hbm", "achieved": ssa_gbs, "peak": PEAK_HBM_GBS,
-                                    "unit": "GB/s", "frac": ssa_gbs / PEAK_HBM_GBS, "traffic": None},
+                       "roofline": decode_roofline(ssa_gbs, ["decode_split_latent grid=65536",
+                                                             "decode_merge<true, 512> grid=131072"]),
                        "timing": f"HIP graph of {reps * n_inst} calls rotating over {n_inst} instances"},
         "full_attn_decode": {"us": full_ms * 1e3, "bytes": full_bytes, "GB/s": full_gbs,
-                             "roofline": {"bound": "hbm", "achieved": full_gbs, "peak": PEAK_HBM_GBS,
-                                          "unit": "GB/s", "frac": full_gbs / PEAK_HBM_GBS,
-                                          "traffic": None}},
+                             "roofline": decode_roofline(full_gbs, ["decode_split_latent grid=524288",
+                                                                    "decode_merge<true, 512> grid=131072"])},
         "ssa_over_full_time": ssa_ms / full_ms,
     }
+    del graph, insts, outs, base, ws_ssa, ws_full
+    free_gpu()
+    return res
 
 
+def bench_decode_ragged(iters: int):
+    """ssa_decode on the ragged workload (65 sequences, 4K-1M tokens, 16 heads,
+    d=128). Its selected pages (~0.5 GB) exceed the Infinity Cache, so back-to-
+    back calls read HBM."""
+    import torch
+    import block_sparse_streaming_amd as ssa
+    from block_sparse_streaming_amd import inputs
+
+    cfg = inputs.CONFIGS[5]
+    pat = inputs.PATTERN
+    dev = "cuda:0"
+    inp = inputs.decode_inputs(cfg, dev)
+    out = torch.empty((cfg.B, cfg.Hq, cfg.d_v), dtype=cfg.dtype, device=dev)
+    ws = torch.empty(ssa.decode_workspace_size(cfg.dtype, cfg.B, cfg.Hq, cfg.Hkv, cfg.d_qk, cfg.d_v,
+                                               inputs.PAGE_SIZE, inp.page_table.shape[1]),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        ssa.decode(inp.q, inp.k_cache, inp.v_cache, inp.page_table, inp.ctx_lens, **pat,
+                   scale=cfg.scale, out=out, workspace=ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ms = time_events(call, iters)
+    sel = [decode_selected_tokens(L, **pat) for L in inp.lens]
+    nbytes = decode_bytes(cfg, inp.lens, sel, inputs.PAGE_SIZE)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": cfg.name, "ssa_decode": {"us": ms * 1e3, "bytes": nbytes, "GB/s": gbs,
+                                                "roofline": decode_roofline(gbs)}}
+    del inp, out, ws
+    free_gpu()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle
+# ---------------------------------------------------------------------------
 def cpu_baseline():
     """The CPU oracle, as it stands, on the prefill workload: every query tile
     of every head (the whole workload is a few seconds of fp64 work on the
@@ -194,11 +309,34 @@ def cpu_baseline():
                       f"{elapsed:.1f} s of fp64 oracle work"}
 
 
+# ---------------------------------------------------------------------------
+# Counter-collection runs
+# ---------------------------------------------------------------------------
+def profile_run(what: str):
+    import torch
+    if what == "prefill":
+        _, step = prefill_setup(2)
+        for _ in range(3):
+            step()
+    elif what == "decode":
+        bench_decode_latent(64)
+    elif what == "copy":
+        n = 1 << 28                                   # 1 GiB of fp32 each way
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--profile", choices=["prefill", "decode", "copy"], default=None)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the 32K prefill (and the CPU oracle)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -209,44 +347,54 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.profile:
+        profile_run(args.profile)
+        return
 
-    cfg, ms, wall, flops, tflops = bench_prefill(args.steps, args.warmup)
-    print(f"# prefill {cfg.name}: {ms:.4f} ms/launch, {tflops:.1f} TFLOP/s", file=sys.stderr,
-          flush=True)
-    dec = bench_decode(200)
-    print(f"# decode: ssa {dec['ssa_decode']['us']:.2f} us ({dec['ssa_decode']['GB/s']:.0f} GB/s), "
-          f"full {dec['full_attn_decode']['us']:.1f} us ({dec['full_attn_decode']['GB/s']:.0f} GB/s)",
-          file=sys.stderr, flush=True)
+    def note(msg):
+        print("# " + msg, file=sys.stderr, flush=True)
+
+    cfg, head = bench_prefill(2, args.steps, args.warmup)
+    note(f"prefill {cfg.name}: {head['ms']:.4f} ms/launch, {head['TFLOP/s']:.1f} TFLOP/s")
+    workloads = {}
+    if not args.headline_only:
+        for cid, steps in ((1, 50), (4, 5)):
+            c, r = bench_prefill(cid, steps, 2)
+            workloads[c.name] = r
+            note(f"prefill {c.name}: {r['ms']:.4f} ms/launch, {r['TFLOP/s']:.1f} TFLOP/s")
+        dec = bench_decode_latent(256)
+        workloads[dec["workload"]] = dec
+        note(f"decode {dec['workload']}: ssa {dec['ssa_decode']['us']:.2f} us "
+             f"({dec['ssa_decode']['GB/s']:.0f} GB/s), full {dec['full_attn_decode']['us']:.1f} us "
+             f"({dec['full_attn_decode']['GB/s']:.0f} GB/s)")
+        rag = bench_decode_ragged(50)
+        workloads[rag["workload"]] = rag
+        note(f"decode {rag['workload']}: ssa {rag['ssa_decode']['us']:.2f} us "
+             f"({rag['ssa_decode']['GB/s']:.0f} GB/s)")
     cpu = cpu_baseline()
-    print(f"# cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads", file=sys.stderr,
-          flush=True)
+    note(f"cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+    from block_sparse_streaming_amd import inputs
     line = {
         "metric": METRIC,
-        "value": tflops,
+        "value": head["TFLOP/s"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.B, "seq_len": cfg.N, "heads": cfg.Hq,
-                   "d_qk": cfg.d_qk, "d_v": cfg.d_v, "pattern": dict(inputs_pattern()),
-                   "algorithmic_flops_per_step": flops},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None},
+                   "d_qk": cfg.d_qk, "d_v": cfg.d_v, "pattern": dict(inputs.PATTERN),
+                   "algorithmic_flops_per_step": head["algorithmic_flops"]},
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
-        "decode": dec,
+        "workloads": workloads,
     }
     print(json.dumps(line), flush=True)
-
-
-def inputs_pattern():
-    from block_sparse_streaming_amd import inputs
-    return inputs.PATTERN
 
 
 if __name__ == "__main__":
