@@ -54,55 +54,57 @@ __device__ __forceinline__ Sel select_tokens(int64_t L, const DecodeArgs &a) {
     return Sel{r1, lo, r1 + n2};
 }
 
-__device__ __forceinline__ int64_t sel_token(const Sel &s, int64_t p) {
-    return p < s.r1_end ? p : s.r2_begin + (p - s.r1_end);
-}
-
-// Element offset of token `tok`'s row (head 0) in a cache with strides `str`.
-__device__ __forceinline__ int64_t token_row(const DecodeArgs &a, int bb, int64_t tok,
-                                             const int64_t *str) {
-    const int64_t page = a.page_table[(int64_t)bb * a.max_pages + tok / a.page_size];
-    return page * str[0] + (tok % a.page_size) * str[1];
-}
-
 // ---------------------------------------------------------------------------
 // VALU split kernel.
 // ---------------------------------------------------------------------------
 constexpr int kValuThreads = 256;
 constexpr int kTpt = 16;                       // lanes per token
 constexpr int kGroups = kValuThreads / kTpt;   // token groups per work-group
-constexpr int kUnroll = 4;                     // tokens per group per step
+
+// E elements of one lane's slice of a cache row, kept as raw 32-bit words.
+template <typename Elem, int E>
+struct RowSlice {
+    static constexpr int kWords = E * (int)sizeof(Elem) / 4;
+    uint32_t w[kWords];
+};
 
 template <typename Elem, int E>
-__device__ __forceinline__ void load_row(const Elem *p, float (&out)[E]) {
-    if constexpr (std::is_same_v<Elem, float>) {
+__device__ __forceinline__ void load_slice(const Elem *p, RowSlice<Elem, E> &r) {
+    constexpr int W = RowSlice<Elem, E>::kWords;
+    if constexpr (W >= 4) {
 #pragma unroll
-        for (int c = 0; c < E / 4; ++c) {
-            const f32x4 w = *(const f32x4 *)(p + 4 * c);
+        for (int c = 0; c < W / 4; ++c) {
+            const u32x4 v = *(const u32x4 *)((const uint32_t *)p + 4 * c);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[4 * c + e] = w[e];
+            for (int e = 0; e < 4; ++e) r.w[4 * c + e] = v[e];
         }
-    } else if constexpr (E == 4) {
-        const u32x2 w = *(const u32x2 *)p;
-        out[0] = bf16_lo(w[0]); out[1] = bf16_hi(w[0]);
-        out[2] = bf16_lo(w[1]); out[3] = bf16_hi(w[1]);
     } else {
-#pragma unroll
-        for (int c = 0; c < E / 8; ++c) {
-            const u32x4 w = *(const u32x4 *)(p + 8 * c);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                out[8 * c + 2 * e] = bf16_lo(w[e]);
-                out[8 * c + 2 * e + 1] = bf16_hi(w[e]);
-            }
-        }
+        const u32x2 v = *(const u32x2 *)p;
+        r.w[0] = v[0];
+        r.w[1] = v[1];
     }
 }
 
+template <typename Elem, int E>
+__device__ __forceinline__ float slice_elem(const RowSlice<Elem, E> &r, int e) {
+    if constexpr (std::is_same_v<Elem, float>) return __uint_as_float(r.w[e]);
+    else return (e & 1) ? bf16_hi(r.w[e >> 1]) : bf16_lo(r.w[e >> 1]);
+}
+
+// One work-group computes one split (up to split_tokens attended tokens) for
+// the G query heads of one kv head. Sixteen lanes share a token (each holds
+// D/16 elements of its key and value rows); the sixteen token groups of the
+// work-group take interleaved positions. A chunk gives every lane TPL tokens
+// whose rows are all requested at once; the next chunk's page ids are read
+// while this chunk's rows are in flight. Each lane keeps its own online
+// softmax state, and the token groups are merged through LDS at the end.
 template <bool kBF16, int D, int G>
 __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeArgs a) {
     using Elem = std::conditional_t<kBF16, uint16_t, float>;
     constexpr int E = D / kTpt;
+    using Slice = RowSlice<Elem, E>;
+    constexpr int kTpl = Slice::kWords <= 4 ? 8 : 32 / Slice::kWords;  // tokens per lane per chunk
+    constexpr int kChunk = kGroups * kTpl;
     __shared__ float sm_m[kGroups][G];
     __shared__ float sm_l[kGroups][G];
     __shared__ float sm_o[kGroups][G][D];
@@ -116,14 +118,46 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
     if (p_begin >= sel.total) return;
     const int64_t p_end = p_begin + a.plan.split_tokens < sel.total ? p_begin + a.plan.split_tokens
                                                                       : sel.total;
+    // Positions and tokens fit in 32 bits (context lengths are int32).
+    const uint32_t up_end = (uint32_t)p_end, ur1 = (uint32_t)sel.r1_end, ur2 = (uint32_t)sel.r2_begin;
+    const uint32_t uP = (uint32_t)a.page_size;
+    const int32_t *ptab = a.page_table + (int64_t)bb * a.max_pages;
 
+    // Token of lane group tg's u-th position in the chunk starting at c0
+    // (clamped to the split's last position; masked later).
+    auto token_of = [&](uint32_t c0, int u) __attribute__((always_inline)) -> uint32_t {
+        uint32_t pp = c0 + (uint32_t)(tg + kGroups * u);
+        pp = pp < up_end ? pp : up_end - 1;
+        return pp < ur1 ? pp : ur2 + (pp - ur1);
+    };
+    int32_t pid[kTpl];
+    auto load_pids = [&](uint32_t c0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kTpl; ++u) pid[u] = ptab[token_of(c0, u) / uP];
+    };
+    Slice kr[kTpl], vr[kTpl];
+    const Elem *kc = (const Elem *)a.kc + g * a.ks[2] + tl * E;
+    const Elem *vc = (const Elem *)a.vc + g * a.vs[2] + tl * E;
+    auto load_rows = [&](uint32_t c0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kTpl; ++u) {
+            const uint32_t tok = token_of(c0, u);
+            const int64_t slot = (int64_t)(tok % uP);
+            load_slice<Elem, E>(kc + pid[u] * a.ks[0] + slot * a.ks[1], kr[u]);
+            load_slice<Elem, E>(vc + pid[u] * a.vs[0] + slot * a.vs[1], vr[u]);
+        }
+    };
+
+    const uint32_t c_first = (uint32_t)p_begin;
+    load_pids(c_first);
     float qv[G][E];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
         const Elem *qp = (const Elem *)a.q + ((int64_t)bb * a.Hq + g * G + hh) * D + tl * E;
-        load_row<Elem, E>(qp, qv[hh]);
+        Slice qs;
+        load_slice<Elem, E>(qp, qs);
 #pragma unroll
-        for (int e = 0; e < E; ++e) qv[hh][e] *= a.scale_log2;
+        for (int e = 0; e < E; ++e) qv[hh][e] = slice_elem<Elem, E>(qs, e) * a.scale_log2;
     }
 
     float m[G], ls[G], acc[G][E];
@@ -135,47 +169,32 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
         for (int e = 0; e < E; ++e) acc[hh][e] = 0.f;
     }
 
-    const Elem *kc = (const Elem *)a.kc + g * a.ks[2] + tl * E;
-    const Elem *vc = (const Elem *)a.vc + g * a.vs[2] + tl * E;
-    for (int64_t p0 = p_begin; p0 < p_end; p0 += kGroups * kUnroll) {
-        float kr[kUnroll][E], vr[kUnroll][E];
-        bool valid[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t pp = p0 + u * kGroups + tg;
-            valid[u] = pp < p_end;
-            if (valid[u]) {
-                const int64_t tok = sel_token(sel, pp);
-                load_row<Elem, E>(kc + token_row(a, bb, tok, a.ks), kr[u]);
-                load_row<Elem, E>(vc + token_row(a, bb, tok, a.vs), vr[u]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) kr[u][e] = vr[u][e] = 0.f;
-            }
-        }
+    for (uint32_t c0 = c_first; c0 < up_end; c0 += kChunk) {
+        load_rows(c0);
+        if (c0 + kChunk < up_end) load_pids(c0 + kChunk);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-            float s[kUnroll];
+            float s[kTpl];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < kTpl; ++u) {
                 float d = 0.f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) d += qv[hh][e] * kr[u][e];
+                for (int e = 0; e < E; ++e) d += qv[hh][e] * slice_elem<Elem, E>(kr[u], e);
                 d += __shfl_xor(d, 8);
                 d += __shfl_xor(d, 4);
                 d += __shfl_xor(d, 2);
                 d += __shfl_xor(d, 1);
-                s[u] = valid[u] ? d : -INFINITY;
+                s[u] = c0 + (uint32_t)(tg + kGroups * u) < up_end ? d : -INFINITY;
             }
             float mx = m[hh];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, s[u]);
+            for (int u = 0; u < kTpl; ++u) mx = fmaxf(mx, s[u]);
             const float m_use = mx == -INFINITY ? 0.f : mx;
             const float alpha = fast_exp2(m[hh] - m_use);
-            float pr[kUnroll];
+            float pr[kTpl];
             float rs = 0.f;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < kTpl; ++u) {
                 pr[u] = fast_exp2(s[u] - m_use);
                 rs += pr[u];
             }
@@ -185,7 +204,7 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
             for (int e = 0; e < E; ++e) {
                 float o = acc[hh][e] * alpha;
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) o += pr[u] * vr[u][e];
+                for (int u = 0; u < kTpl; ++u) o += pr[u] * slice_elem<Elem, E>(vr[u], e);
                 acc[hh][e] = o;
             }
         }
