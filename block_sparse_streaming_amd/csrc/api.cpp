@@ -127,7 +127,8 @@ ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, co
             return SSA_ERR_UNSUPPORTED;
     }
     if ((int64_t)batch * heads_q > kInt32Max || (int64_t)heads_kv * plan.head_chunks > 65535 ||
-        batch > 65535 || heads_q > 65535)
+        batch > 65535 || heads_q > 65535 ||
+        (int64_t)plan.max_splits * heads_kv * plan.head_chunks * batch > kInt32Max)  // linear work-group ids
         return SSA_ERR_UNSUPPORTED;
     const WorkspaceLayout wl = workspace_layout(batch, heads_q, d_v, plan);
     if (!workspace || !aligned16(workspace) || workspace_bytes < wl.total) return SSA_ERR_WORKSPACE;

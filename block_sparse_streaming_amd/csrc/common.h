@@ -104,6 +104,17 @@ __device__ __forceinline__ void dma16_untracked(const void *src, uint32_t lds_wa
         : "memory");
 }
 
+// max(x, x from lane ^ 16) and max(x, x from lane ^ 32) on the VALU (gfx950
+// permlane swaps), instead of an LDS round trip through ds_bpermute.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const lds_void *)p;

@@ -46,7 +46,7 @@ struct Sel {
 __device__ __forceinline__ Sel select_tokens(int64_t L, const DecodeArgs &a) {
     if (a.full) return Sel{L, L, L};
     const int64_t b = a.block, sb = (int64_t)a.sink * b;
-    const int64_t qb = (L - 1) / b;
+    const int64_t qb = (int64_t)((uint32_t)(L - 1) / (uint32_t)a.block);  // L <= INT32_MAX
     const int64_t r1 = sb < L ? sb : L;
     const int64_t lo0 = (qb - a.local + 1) * b;
     const int64_t lo = lo0 > sb ? lo0 : sb;
@@ -276,9 +276,13 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     __shared__ int32_t pids[kLatMaxPages];
     __shared__ int64_t rowtab[4][kLatRowsPerWave];
 
-    const int split = blockIdx.x;
-    const int hc = blockIdx.y % a.plan.head_chunks, g = blockIdx.y / a.plan.head_chunks;
-    const int bb = blockIdx.z;
+    // Work-groups of one XCD (own L2) take whole sequences, so the splits of a
+    // sequence share q in that L2.
+    const int nx = gridDim.x, ny = gridDim.y;
+    const int lin = xcd_remap(blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z), nx * ny * gridDim.z);
+    const int split = lin % nx;
+    const int hcg = (lin / nx) % ny, bb = lin / (nx * ny);
+    const int hc = hcg % a.plan.head_chunks, g = hcg / a.plan.head_chunks;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, kg = lane >> 4;
@@ -411,8 +415,7 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
         scores(buf, c, s);
         float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+        mx = max_xor32(max_xor16(mx)) * a.scale_log2;
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kLatSlack)) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = fast_exp2(m_run - m_new);  // 0 on the first chunk
@@ -527,6 +530,30 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
     }
     const int64_t slot0 = (int64_t)row * a.plan.max_splits;
     const float *wl = a.ws_lse + slot0;
+    const float *wo = a.ws_o + slot0 * D + E * lane;
+
+    // Partial rows of splits s0 .. s0+7 (clamped to the last split).
+    float part[kMergeBatch][E];
+    auto load_batch = [&](int s0, int nb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const int s = s0 + u < nb ? s0 + u : nb - 1;
+            const float *src = wo + (int64_t)s * D;
+            if constexpr (E >= 4) {
+#pragma unroll
+                for (int e4 = 0; e4 < E / 4; ++e4) {
+                    const f32x4 v = *(const f32x4 *)(src + 4 * e4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) part[u][4 * e4 + e] = v[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) part[u][e] = src[e];
+            }
+        }
+    };
+    // The first batch is requested before the weights are known.
+    load_batch(0, ns < 64 ? ns : 64);
     float M = -INFINITY;
     for (int s = lane; s < ns; s += 64) M = fmaxf(M, wl[s]);
 #pragma unroll
@@ -537,38 +564,24 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
     for (int o = 32; o >= 1; o >>= 1) Z += __shfl_xor(Z, o);
     const float inv = 1.f / Z;
 
-    const float *wo = a.ws_o + slot0 * D + E * lane;
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
     for (int s64 = 0; s64 < ns; s64 += 64) {
         const float wlane = s64 + lane < ns ? fast_exp2(wl[s64 + lane] - M) * inv : 0.f;
         const int nb = ns - s64 < 64 ? ns - s64 : 64;
+        if (s64 > 0) load_batch(0, nb);
         for (int s0 = 0; s0 < nb; s0 += kMergeBatch) {
-            float part[kMergeBatch][E];
+            if (s0 > 0) load_batch(s0, nb);
 #pragma unroll
             for (int u = 0; u < kMergeBatch; ++u) {
-                const int s = s0 + u < nb ? s0 + u : nb - 1;
-                const float *src = wo + (int64_t)(s64 + s) * D;
-#pragma unroll
-                for (int e4 = 0; e4 < (E + 3) / 4; ++e4) {
-                    if constexpr (E >= 4) {
-                        const f32x4 v = *(const f32x4 *)(src + 4 * e4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) part[u][4 * e4 + e] = v[e];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < E; ++e) part[u][e] = src[e];
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kMergeBatch; ++u) {
-                const float wf = s0 + u < nb ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlane), s0 + u)) : 0.f;
+                const float wf =
+                    s0 + u < nb ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlane), s0 + u)) : 0.f;
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(wf, part[u][e], acc[e]);
             }
         }
+        wo += (int64_t)64 * D;
     }
     if constexpr (kBF16) {
 #pragma unroll
