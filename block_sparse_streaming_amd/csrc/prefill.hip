@@ -119,7 +119,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     __shared__ __attribute__((aligned(1024))) uint16_t v_buf0[kBN * DV];
     __shared__ __attribute__((aligned(1024))) uint16_t v_buf1[kBN * DV];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
     const int l32 = lane & 31, hi = lane >> 5;
 
     const int wg = xcd_remap(blockIdx.x, a.total_wgs);
@@ -152,29 +153,53 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
 
     // Direct transfers: lane slot p of transfer n covers tile row p / C at
     // physical unit p % C, which holds logical unit (p % C) ^ swz(row). Byte
-    // offsets from the sub-tile's first row; rows past the range end re-read
-    // the range's last row (masked later), so nothing outside the tile's
-    // attended key set is touched.
+    // offsets from the sub-tile's first row, computed once per lane; in a
+    // sub-tile cut short by its range end, rows past the end re-read the
+    // range's last row (masked later), so nothing outside the tile's attended
+    // key set is touched.
     auto dma_off = [&](int p, int C, int swz, int stride, int rows_valid) -> uint32_t {
         int row = p / C;
         const int unit = (p % C) ^ swz;
         row = row < rows_valid ? row : rows_valid - 1;
         return (uint32_t)(row * stride + unit * 8) * 2u;
     };
+    // Full sub-tiles reuse offsets computed once, when the registers allow it
+    // (d_qk = 192 has too many transfers per wave and recomputes them).
+    constexpr bool kKeepOffsets = NIK + NIV <= 8;
+    uint32_t koff[NIK], voff[NIV];
+    if constexpr (kKeepOffsets) {
+#pragma unroll
+        for (int n = 0; n < NIK; ++n) {
+            const int p = (wave * NIK + n) * 64 + lane;
+            koff[n] = dma_off(p, CK, k_swz<CK>(p / CK), ks1, kBN);
+        }
+#pragma unroll
+        for (int n = 0; n < NIV; ++n) {
+            const int p = (wave * NIV + n) * 64 + lane;
+            voff[n] = dma_off(p, CV, v_swz<CV>(p / CV), vs1, kBN);
+        }
+    }
     auto issue = [&](int t, uint16_t *kb, uint16_t *vb) {
         const SubTile st = sub_tile(tr, t);
         const int rows_valid = st.re - st.j0;
         const char *kt = (const char *)(kbase + (int64_t)st.j0 * a.ks[1]);
         const char *vt = (const char *)(vbase + (int64_t)st.j0 * a.vs[1]);
+        if (kKeepOffsets && rows_valid >= kBN) {
 #pragma unroll
-        for (int n = 0; n < NIK; ++n) {
-            const int p = (wave * NIK + n) * 64 + lane;
-            dma16(kt + dma_off(p, CK, k_swz<CK>(p / CK), ks1, rows_valid), kb + (wave * NIK + n) * 512);
-        }
+            for (int n = 0; n < NIK; ++n) dma16(kt + koff[n], kb + (wave * NIK + n) * 512);
 #pragma unroll
-        for (int n = 0; n < NIV; ++n) {
-            const int p = (wave * NIV + n) * 64 + lane;
-            dma16(vt + dma_off(p, CV, v_swz<CV>(p / CV), vs1, rows_valid), vb + (wave * NIV + n) * 512);
+            for (int n = 0; n < NIV; ++n) dma16(vt + voff[n], vb + (wave * NIV + n) * 512);
+        } else {
+#pragma unroll
+            for (int n = 0; n < NIK; ++n) {
+                const int p = (wave * NIK + n) * 64 + lane;
+                dma16(kt + dma_off(p, CK, k_swz<CK>(p / CK), ks1, rows_valid), kb + (wave * NIK + n) * 512);
+            }
+#pragma unroll
+            for (int n = 0; n < NIV; ++n) {
+                const int p = (wave * NIV + n) * 64 + lane;
+                dma16(vt + dma_off(p, CV, v_swz<CV>(p / CV), vs1, rows_valid), vb + (wave * NIV + n) * 512);
+            }
         }
     };
 
@@ -205,8 +230,23 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
                     (uint32_t)((tr_col & 4) << 1);
     const int jl = 4 * hi;  // key offset of this lane's accumulator rows
 
+    // Rows of this wave: r_first .. r_last (clamped to the sequence), and the
+    // window starts of its first and last rows.
+    const int r_first = tr.q0 + wave * 32;
+    const int r_last = r_first + 31 < a.N - 1 ? r_first + 31 : a.N - 1;
+    const int lo_first_w = local_start(a, r_first), lo_last_w = local_start(a, r_last);
+
     auto compute = [&](int t, const uint16_t *kb, const uint16_t *vb) {
         const SubTile st = sub_tile(tr, t);
+        // What this sub-tile means for this wave's rows (wave-uniform): keys
+        // of a local sub-tile lie past the sink range, so there a key is
+        // attended iff lo_i <= j <= i; in the sink range iff j <= i.
+        const bool local = t >= tr.n_sink;
+        const int kend = st.j0 + kBN < st.re ? st.j0 + kBN : st.re;  // exclusive
+        if (r_first >= a.N || st.j0 > r_last || (local && kend <= lo_first_w)) return;  // nothing attended
+        const bool full = st.j0 + kBN <= st.re && (!local || st.j0 >= lo_last_w);
+        const bool no_mask = full && st.j0 + kBN - 1 <= r_first;  // every key <= every row
+        const bool causal_only = full && !no_mask;                // only j <= i can fail
         // Re-derive the lane offsets here (the empty asm hides their origin)
         // so that address arithmetic is not hoisted out of the loop into
         // registers that would stay live across it.
@@ -241,7 +281,17 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         // (in log2 units): until then p <= 2^kRescaleSlack and the O/l rescale
         // is skipped. O and l always use the same m_run, so O / l is exact.
         float mx = -INFINITY;
-        if (st.need_mask) {
+        if (causal_only) {
+            const int d0 = i - (st.j0 + jl);  // key offset k is attended iff k <= d0
+#pragma unroll
+            for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float x = kbk * 32 + 8 * (r >> 2) + (r & 3) <= d0 ? sacc[kbk][r] : -INFINITY;
+                    sacc[kbk][r] = x;
+                    mx = fmaxf(mx, x);
+                }
+        } else if (!no_mask) {
             const int jb = st.j0 + jl;
 #pragma unroll
             for (int kbk = 0; kbk < 2; ++kbk)
@@ -259,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kbk][r]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+        mx = max_xor32(mx) * a.scale_log2;
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
