@@ -254,10 +254,15 @@ constexpr int kLatMaxPages = kDecodeLatentMaxPages;   // page ids of one split k
 constexpr float kLatSlack = 8.f;                      // lazy-rescale slack (log2 units)
 static_assert(kLatDma * 64 == kLatRowsPerWave * kLatUnits, "a wave moves whole rows");
 
-// XOR swizzle of the 16-byte units of latent row r (1152 B = 128 mod 256):
-// the 16 rows read at one unit by a score-operand read, and the 8 rows x 2
-// units read by a half-wave's transpose read, both land in 16 bank groups.
-__device__ __forceinline__ int lat_swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+// XOR swizzle of the 16-byte units of latent row r (1152 B, a multiple of
+// 128 B, so unswizzled rows all start in the same banks). A linear map of the
+// low four row bits, chosen so that both access patterns are conflict-free
+// whether the LDS serves 128 or 256 bytes per cycle: 8 or 16 consecutive
+// rows read at one unit (score operand), and 4 or 8 consecutive rows x 2
+// units (transpose reads). Depends on r mod 16 only.
+__device__ __forceinline__ int lat_swz(int r) {
+    return ((r >> 2) & 1) | (r & 2) | (((r ^ (r >> 2) ^ (r >> 3)) & 1) << 2);
+}
 
 // One work-group computes one split (up to split_tokens attended tokens of
 // one sequence) for up to 64 query heads of one kv head; wave w owns heads
