@@ -93,6 +93,46 @@ def recorded_traffic(keys: list[str]):
     return total
 
 
+MEASURED = {}   # attainable ceilings measured on this GPU at start-up (see measure_ceilings)
+
+
+def measure_ceilings():
+    """What this GPU sustains right now through vendor libraries, as a second
+    reference beside the published peaks: a 16384^3 bf16 GEMM (hipBLASLt) for
+    the matrix cores, and a memory-bound skinny GEMM reading a 4 GiB operand
+    for HBM (2 * 4 GiB / time counts the operand only)."""
+    import torch
+    dev = "cuda:0"
+    n = 16384
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    for _ in range(2):
+        torch.mm(a, b)
+    ms = time_events(lambda: torch.mm(a, b), 5)
+    gemm = 2 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b
+    x = torch.ones((1 << 18, 1 << 13), dtype=torch.bfloat16, device=dev)   # 4 GiB
+    w = torch.ones((1 << 13, 16), dtype=torch.bfloat16, device=dev)
+    for _ in range(2):
+        torch.mm(x, w)
+    ms = time_events(lambda: torch.mm(x, w), 10)
+    hbm = x.numel() * 2 / (ms * 1e-3) / 1e9
+    del x, w
+    free_gpu()
+    MEASURED.update({"bf16_gemm_tflops": gemm, "hbm_read_gbs": hbm,
+                     "how": "torch.mm bf16 16384^3 (hipBLASLt); torch.mm [262144x8192]x[8192x16] bf16, "
+                            "operand bytes / time"})
+    return MEASURED
+
+
+def with_measured(roof: dict) -> dict:
+    key = "bf16_gemm_tflops" if roof["unit"] == "TFLOP/s" else "hbm_read_gbs"
+    if key in MEASURED and not (roof["unit"] == "TFLOP/s" and roof["peak"] != PEAK_BF16_TFLOPS):
+        roof["measured_peak"] = MEASURED[key]
+        roof["frac_of_measured"] = roof["achieved"] / MEASURED[key]
+    return roof
+
+
 def free_gpu():
     import gc
     import torch
@@ -137,9 +177,9 @@ def bench_prefill(cfg_id: int, steps: int, warmup: int):
     grid = -(-cfg.N // 128) * cfg.Hq * cfg.B * 256
     res = {"workload": cfg.name, "ms": ms, "steps": steps, "algorithmic_flops": flops,
            "TFLOP/s": tflops,
-           "roofline": {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
-                        "frac": tflops / peak,
-                        "traffic": recorded_traffic([f"{kernel} grid={grid}"])}}
+           "roofline": with_measured({"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                                      "frac": tflops / peak,
+                                      "traffic": recorded_traffic([f"{kernel} grid={grid}"])})}
     del step
     free_gpu()
     return cfg, res
@@ -159,9 +199,9 @@ def decode_bytes(cfg, lens, selected, page_size: int) -> int:
 
 
 def decode_roofline(gbs: float, traffic_keys=None) -> dict:
-    return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": gbs / PEAK_HBM_GBS,
-            "traffic": recorded_traffic(traffic_keys) if traffic_keys else None}
+    return with_measured({"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": gbs / PEAK_HBM_GBS,
+                          "traffic": recorded_traffic(traffic_keys) if traffic_keys else None})
 
 
 def bench_decode_latent(iters: int):
@@ -354,6 +394,10 @@ def main():
     def note(msg):
         print("# " + msg, file=sys.stderr, flush=True)
 
+    if not args.headline_only:
+        m = measure_ceilings()
+        note(f"measured ceilings: bf16 GEMM {m['bf16_gemm_tflops']:.0f} TFLOP/s, "
+             f"HBM read {m['hbm_read_gbs']:.0f} GB/s")
     cfg, head = bench_prefill(2, args.steps, args.warmup)
     note(f"prefill {cfg.name}: {head['ms']:.4f} ms/launch, {head['TFLOP/s']:.1f} TFLOP/s")
     workloads = {}
@@ -392,6 +436,7 @@ def main():
                    "algorithmic_flops_per_step": head["algorithmic_flops"]},
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "measured_ceilings": dict(MEASURED),
         "workloads": workloads,
     }
     print(json.dumps(line), flush=True)
