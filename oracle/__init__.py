@@ -55,6 +55,9 @@ def _load():
         lib.oracle_decode_paged.restype = i32
         lib.oracle_decode_paged.argtypes = [i32, p, p, p, p, p, i64, p, i64, p, i32, i32, i32,
                                             i32, i32, i32, i32, i32, i32, i32, dbl, p, p]
+        lib.oracle_ssa_backward.restype = i32
+        lib.oracle_ssa_backward.argtypes = [i32, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32,
+                                            i32, i32, i32, i32, i32, dbl, p, i64, p, p, p]
         lib.oracle_max_threads.restype = i32
         lib.oracle_set_threads.argtypes = [i32]
         _lib = lib
@@ -153,3 +156,39 @@ def decode_paged(q, k_cache, v_cache, page_table, ctx_lens, *, block=128, sink=1
     if rc != 0:
         raise ValueError("oracle_decode_paged rejected its arguments")
     return o, lse
+
+
+def backward(q, k, v, dout, *, block=128, sink=1, local=7, scale, full=False, rows=None):
+    """Gradients of the prefill operator for the upstream gradient ``dout``.
+
+    q [B, N, Hq, d_qk], k [B, N, Hkv, d_qk], v [B, N, Hkv, d_v], dout
+    [B, N, Hq, d_v], all of one element type. Returns ``(dq, dk, dv)`` in
+    float64: dq [B, R, Hq, d_qk] for the evaluated rows, dk / dv [B, N, Hkv, d]
+    holding the contributions of those rows (all rows when ``rows`` is None).
+    """
+    lib = _load()
+    elem = _elem(q)
+    if _elem(k) != elem or _elem(v) != elem or _elem(dout) != elem:
+        raise TypeError("q, k, v, dout must share one element type")
+    B, N, Hq, d_qk = q.shape
+    Bk, Nk, Hkv, d_qk2 = k.shape
+    Bv, Nv, Hkv2, d_v = v.shape
+    if (Bk, Nk, d_qk2) != (B, N, d_qk) or (Bv, Nv, Hkv2) != (B, N, Hkv):
+        raise ValueError("shape mismatch")
+    if dout.shape != (B, N, Hq, d_v):
+        raise ValueError("dout shape mismatch")
+    rows_arr = None
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    R = N if rows_arr is None else rows_arr.size
+    dq = np.empty((B, R, Hq, d_qk), dtype=np.float64)
+    dk = np.empty((B, N, Hkv, d_qk), dtype=np.float64)
+    dv = np.empty((B, N, Hkv, d_v), dtype=np.float64)
+    qs, ks, vs, ds = _strides(q, 3), _strides(k, 3), _strides(v, 3), _strides(dout, 3)
+    rc = lib.oracle_ssa_backward(elem, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(qs), _ptr(ks),
+                                 _ptr(vs), _ptr(ds), B, N, Hq, Hkv, d_qk, d_v, block, sink, local,
+                                 int(full), float(scale), _ptr(rows_arr), R, _ptr(dq), _ptr(dk),
+                                 _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle_ssa_backward rejected its arguments")
+    return dq, dk, dv

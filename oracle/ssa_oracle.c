@@ -38,6 +38,12 @@
  * Decode: the newest token sits at position L - 1 of a context of L tokens
  * whose keys and values (the new token's included) are already in a paged
  * cache; token t lives in page page_table[t / P] at slot t % P.
+ *
+ * Backward: the pages train with SSA in place (the digest's section 01,
+ * part (1), the training paragraph after the SSA output, and part (2), the
+ * mid-training and post-training of the sparsified model), so the
+ * gradients of q, k and v are those of the same operator, by the chain rule
+ * through the masked softmax; oracle_ssa_backward writes them out per row.
  */
 #include <math.h>
 #include <stdint.h>
@@ -277,6 +283,125 @@ int oracle_decode_paged(int elem, const void *q, const void *k_cache,
         free(vrow);
         free(score);
         free(qd);
+    }
+    return 0;
+}
+
+/* Backward of the prefill operator: the gradients of q, k and v for an
+ * upstream gradient dout = dL/do. The pages train with SSA in place
+ * (mid-training and post-training run on the sparse layers), so the operator
+ * is differentiated as written, with no approximation. For query row i with
+ * attended keys A(i) and weights w_j (recomputed here in double):
+ *   g_j   = <dout_i, v_j>                      (dL/dw_j)
+ *   ds_j  = w_j * (g_j - sum_{j' in A(i)} w_j' g_j')   (softmax Jacobian)
+ *   dq_i  = scale * sum_j ds_j k_j
+ *   dk_j += scale * ds_j q_i
+ *   dv_j += w_j dout_i
+ * A kv head collects these from every query head of its group.
+ *   q, k, v, dout: as for oracle_ssa_prefill; dout [B, N, Hq, d_v] with
+ *   element strides do_str (batch, token, head).
+ *   rows: the query positions whose terms are taken (NULL: all N); dk and dv
+ *   then hold those rows' share only, which makes sampled checks of large
+ *   shapes cheap.
+ *   dq [B, R, Hq, d_qk], dk [B, N, Hkv, d_qk], dv [B, N, Hkv, d_v]: contiguous
+ *   doubles, overwritten.
+ * Work is split over (batch, kv head): one thread owns the dk/dv rows it adds
+ * to, and adds in a fixed order. Returns 0, or -1 on a bad argument. */
+int oracle_ssa_backward(int elem, const void *q, const void *k, const void *v,
+                        const void *dout, const int64_t *q_str,
+                        const int64_t *k_str, const int64_t *v_str,
+                        const int64_t *do_str, int B, int N, int Hq, int Hkv,
+                        int d_qk, int d_v, int block, int sink, int local,
+                        int full, double scale, const int64_t *rows,
+                        int64_t n_rows, double *dq, double *dk, double *dv)
+{
+    if (B < 0 || N < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d_qk <= 0 ||
+        d_v <= 0 || block < 1 || (!full && (sink < 0 || local < 1)))
+        return -1;
+    int64_t R = rows ? n_rows : N;
+    for (int64_t r = 0; r < R; ++r)
+        if (rows && (rows[r] < 0 || rows[r] >= N))
+            return -1;
+    memset(dq, 0, sizeof(double) * (size_t)B * R * Hq * d_qk);
+    memset(dk, 0, sizeof(double) * (size_t)B * N * Hkv * d_qk);
+    memset(dv, 0, sizeof(double) * (size_t)B * N * Hkv * d_v);
+    int64_t group = Hq / Hkv;
+    int64_t tasks = (int64_t)B * Hkv;
+    size_t cap = (size_t)(N > 0 ? N : 1);
+
+#pragma omp parallel
+    {
+        int64_t *keys = malloc(sizeof(int64_t) * cap);
+        double *score = malloc(sizeof(double) * cap);
+        double *w = malloc(sizeof(double) * cap);
+        double *gw = malloc(sizeof(double) * cap);
+        double *qd = malloc(sizeof(double) * (size_t)d_qk);
+        double *dod = malloc(sizeof(double) * (size_t)d_v);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < tasks; ++t) {
+            int64_t g = t % Hkv, bb = t / Hkv;
+            for (int64_t h = g * group; h < (g + 1) * group; ++h) {
+                for (int64_t r = 0; r < R; ++r) {
+                    int64_t i = rows ? rows[r] : r;
+                    int64_t qoff = bb * q_str[0] + i * q_str[1] + h * q_str[2];
+                    int64_t dooff = bb * do_str[0] + i * do_str[1] + h * do_str[2];
+                    for (int d = 0; d < d_qk; ++d)
+                        qd[d] = elem_at(q, elem, qoff + d);
+                    for (int d = 0; d < d_v; ++d)
+                        dod[d] = elem_at(dout, elem, dooff + d);
+                    int64_t n = attended_keys(i, block, sink, local, full, keys);
+
+                    /* Forward weights of row i. */
+                    double m = -INFINITY;
+                    for (int64_t a = 0; a < n; ++a) {
+                        int64_t koff = bb * k_str[0] + keys[a] * k_str[1] + g * k_str[2];
+                        double acc = 0.0;
+                        for (int d = 0; d < d_qk; ++d)
+                            acc += qd[d] * elem_at(k, elem, koff + d);
+                        score[a] = scale * acc;
+                        if (score[a] > m)
+                            m = score[a];
+                    }
+                    double denom = 0.0;
+                    for (int64_t a = 0; a < n; ++a)
+                        denom += exp(score[a] - m);
+                    for (int64_t a = 0; a < n; ++a)
+                        w[a] = exp(score[a] - m) / denom;
+
+                    /* dL/dw_j and the weighted mean it is measured from. */
+                    double mean = 0.0;
+                    for (int64_t a = 0; a < n; ++a) {
+                        int64_t voff = bb * v_str[0] + keys[a] * v_str[1] + g * v_str[2];
+                        double acc = 0.0;
+                        for (int d = 0; d < d_v; ++d)
+                            acc += dod[d] * elem_at(v, elem, voff + d);
+                        gw[a] = acc;
+                        mean += w[a] * acc;
+                    }
+
+                    double *dqi = dq + ((bb * R + r) * Hq + h) * d_qk;
+                    for (int64_t a = 0; a < n; ++a) {
+                        int64_t j = keys[a];
+                        double ds = w[a] * (gw[a] - mean);
+                        int64_t koff = bb * k_str[0] + j * k_str[1] + g * k_str[2];
+                        double *dkj = dk + ((bb * N + j) * Hkv + g) * d_qk;
+                        double *dvj = dv + ((bb * N + j) * Hkv + g) * d_v;
+                        for (int d = 0; d < d_qk; ++d) {
+                            dqi[d] += scale * ds * elem_at(k, elem, koff + d);
+                            dkj[d] += scale * ds * qd[d];
+                        }
+                        for (int d = 0; d < d_v; ++d)
+                            dvj[d] += w[a] * dod[d];
+                    }
+                }
+            }
+        }
+        free(keys);
+        free(score);
+        free(w);
+        free(gw);
+        free(qd);
+        free(dod);
     }
     return 0;
 }
