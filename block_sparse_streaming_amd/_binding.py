@@ -20,8 +20,8 @@ SSA_F32 = 0
 SSA_BF16 = 1
 
 # Exported symbols, in the order include/ssa.h declares them.
-EXPORTS = ("ssa_prefill", "ssa_decode", "full_attn_decode", "ssa_decode_workspace_size",
-           "ssa_status_string")
+EXPORTS = ("ssa_prefill", "ssa_prefill_backward", "ssa_prefill_backward_workspace_size",
+           "ssa_decode", "full_attn_decode", "ssa_decode_workspace_size", "ssa_status_string")
 
 
 class SSAError(RuntimeError):
@@ -55,6 +55,13 @@ def load_library() -> ctypes.CDLL:
     lib.ssa_prefill.restype = ctypes.c_int
     lib.ssa_prefill.argtypes = [ctypes.c_int, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                 i64p, i64p, i64p, i64p, Pattern, f32, p]
+    lib.ssa_prefill_backward.restype = ctypes.c_int
+    lib.ssa_prefill_backward.argtypes = [ctypes.c_int, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
+                                         i32, i32, i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p,
+                                         p, sz, Pattern, f32, p]
+    lib.ssa_prefill_backward_workspace_size.restype = sz
+    lib.ssa_prefill_backward_workspace_size.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32,
+                                                        Pattern]
     lib.ssa_decode.restype = ctypes.c_int
     lib.ssa_decode.argtypes = [ctypes.c_int, p, p, p, i64p, i64p, p, i32, p, i32, i32, i32, i32, i32,
                                i32, p, p, p, sz, Pattern, f32, p]
@@ -136,6 +143,59 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, block: int = 1
                            d_v, _strides3(q), _strides3(k), _strides3(v), _strides3(out),
                            Pattern(block, sink, local), float(scale), _stream(q.device)))
     return (out, lse) if return_lse else out
+
+
+def backward_workspace_size(dtype: torch.dtype, batch: int, seq_len: int, heads_q: int,
+                            heads_kv: int, d_qk: int, d_v: int, *, block: int = 128, sink: int = 1,
+                            local: int = 7) -> int:
+    """Bytes of workspace ssa_prefill_backward needs (0 if it rejects the shape)."""
+    code = SSA_BF16 if dtype == torch.bfloat16 else SSA_F32
+    return int(load_library().ssa_prefill_backward_workspace_size(
+        code, batch, seq_len, heads_q, heads_kv, d_qk, d_v, Pattern(block, sink, local)))
+
+
+def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                     lse: torch.Tensor, dout: torch.Tensor, *, block: int = 128, sink: int = 1,
+                     local: int = 7, scale: float | None = None, dq=None, dk=None, dv=None,
+                     workspace=None):
+    """ssa_prefill_backward: gradients (dq, dk, dv) of ``prefill`` for the
+    upstream gradient ``dout``, given the forward's output ``o`` and its
+    ``lse`` [B, Hq, N] (``prefill(..., return_lse=True)``)."""
+    lib = load_library()
+    _on_gpu(q, k, v, o, lse, dout)
+    dt = _dtype_code(q)
+    for t in (k, v, o, dout):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, o, dout must share one dtype")
+    B, N, Hq, d_qk = q.shape
+    Hkv, d_v = k.shape[2], v.shape[3]
+    if k.shape != (B, N, Hkv, d_qk) or v.shape != (B, N, Hkv, d_v):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if o.shape != (B, N, Hq, d_v) or dout.shape != (B, N, Hq, d_v):
+        raise ValueError("o and dout must be [B, N, Hq, d_v]")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    for got, want in ((dq, q), (dk, k), (dv, v)):
+        if got.shape != want.shape or got.dtype != want.dtype:
+            raise ValueError("gradient outputs must match their inputs' shape and dtype")
+    _on_gpu(dq, dk, dv)
+    need = backward_workspace_size(q.dtype, B, N, Hq, Hkv, d_qk, d_v, block=block, sink=sink,
+                                   local=local)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _on_gpu(workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.ssa_prefill_backward(
+        dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, N, Hq, Hkv, d_qk, d_v, _strides3(q), _strides3(k), _strides3(v), _strides3(o),
+        _strides3(dout), _strides3(dq), _strides3(dk), _strides3(dv), _ptr(workspace), ws_bytes,
+        Pattern(block, sink, local), float(scale), _stream(q.device)))
+    return dq, dk, dv
 
 
 def decode_workspace_size(dtype: torch.dtype, batch: int, heads_q: int, heads_kv: int, d_qk: int,

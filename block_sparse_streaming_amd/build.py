@@ -16,12 +16,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssa.so")
-SOURCES = ["api.cpp", "prefill.hip", "decode.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "backward.hip", "decode.hip"]
 ARCH = "gfx950"
-# decode.hip's only MFMA kernel keeps its output accumulators in VGPRs (their
-# rescale is VALU work) and its read-only q operand in AGPRs; the VGPR form of
-# MFMA lets the compiler do that without copying the accumulators each chunk.
-EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# decode.hip's MFMA kernel and the backward kernels keep their accumulators in
+# VGPRs (scores feed VALU work) and their read-only operands in AGPRs; the VGPR
+# form of MFMA lets the compiler do that without copying accumulators around.
+EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -162,6 +162,48 @@ ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, co
     return ssa::launch_decode(dtype == SSA_BF16, d_qk, d_v, a, stream) == hipSuccess ? SSA_OK : SSA_ERR_HIP;
 }
 
+// Work plan of a backward call (shapes only).
+struct BackwardPlan {
+    int64_t n_pad, num_qtiles, sink_tiles, sink_rows, chunk_rows, n_chunks;
+    int64_t dq_wgs, dkv_wgs, fin_wgs;
+    size_t rowstat_bytes, part_offset, total;
+};
+
+// Rows of a key tile that holds sink keys are cut into chunks of about four
+// times the rows a key past the sink is attended by (l*b), so that a chunk's
+// work is a small multiple of an ordinary key tile's.
+BackwardPlan backward_plan(int32_t batch, int32_t seq_len, int32_t heads_q, int32_t heads_kv,
+                           int32_t d_qk, int32_t d_v, const ssa_pattern &p) {
+    BackwardPlan b;
+    b.n_pad = ((int64_t)seq_len + 127) / 128 * 128;
+    b.num_qtiles = b.n_pad / 128;
+    const int64_t sb = (int64_t)p.sink * p.block;
+    const int64_t sink_keys = sb < seq_len ? sb : seq_len;
+    b.sink_tiles = (sink_keys + 127) / 128;
+    b.sink_rows = b.sink_tiles * 128 < seq_len ? b.sink_tiles * 128 : seq_len;
+    int64_t span = (int64_t)p.local * p.block;
+    span = span < b.n_pad ? span : b.n_pad;
+    span = (span + 127) / 128 * 128;
+    int64_t chunk = 4 * (span < 128 ? 128 : span);
+    b.chunk_rows = chunk < b.n_pad ? chunk : b.n_pad;
+    b.n_chunks = b.sink_tiles > 0 ? (seq_len + b.chunk_rows - 1) / b.chunk_rows : 0;
+    b.dq_wgs = b.num_qtiles * heads_q * batch;
+    b.dkv_wgs = (b.sink_tiles * b.n_chunks + (b.num_qtiles - b.sink_tiles)) * heads_kv * batch;
+    const int64_t fin_items = (int64_t)batch * heads_kv * b.sink_rows * ((d_qk + d_v) / 4);
+    b.fin_wgs = (fin_items + 255) / 256;
+    b.rowstat_bytes = (size_t)batch * heads_q * b.n_pad * 2 * sizeof(float);
+    b.part_offset = (b.rowstat_bytes + 255) / 256 * 256;
+    b.total = b.part_offset +
+              (size_t)b.n_chunks * batch * heads_kv * b.sink_rows * (d_qk + d_v) * sizeof(float);
+    return b;
+}
+
+bool backward_shape_ok(ssa_dtype dtype, int32_t batch, int32_t seq_len, int32_t heads_q,
+                       int32_t heads_kv, int32_t d_qk, int32_t d_v, const ssa_pattern &p) {
+    return dtype_ok(dtype) && batch >= 0 && seq_len >= 0 && heads_q >= 1 && heads_kv >= 1 &&
+           heads_q % heads_kv == 0 && d_qk >= 1 && d_v >= 1 && pattern_ok(p);
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,6 +263,95 @@ ssa_status ssa_prefill(ssa_dtype dtype, const void *q, const void *k, const void
     a.total_wgs = (int32_t)total;
     return ssa::launch_prefill(dtype == SSA_BF16, d_qk, d_v, a, stream) == hipSuccess ? SSA_OK
                                                                                      : SSA_ERR_HIP;
+}
+
+ssa_status ssa_prefill_backward(ssa_dtype dtype, const void *q, const void *k, const void *v,
+                                const void *o, const float *lse, const void *dout, void *dq,
+                                void *dk, void *dv, int32_t batch, int32_t seq_len,
+                                int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                                const int64_t q_strides[3], const int64_t k_strides[3],
+                                const int64_t v_strides[3], const int64_t o_strides[3],
+                                const int64_t do_strides[3], const int64_t dq_strides[3],
+                                const int64_t dk_strides[3], const int64_t dv_strides[3],
+                                void *workspace, size_t workspace_bytes, ssa_pattern pattern,
+                                float scale, hipStream_t stream) {
+    if (!backward_shape_ok(dtype, batch, seq_len, heads_q, heads_kv, d_qk, d_v, pattern))
+        return SSA_ERR_INVALID_ARG;
+    if (!(std::isfinite(scale) && scale > 0.f)) return SSA_ERR_INVALID_ARG;
+    const int eb = elem_bytes(dtype);
+    const int64_t *all_strides[8] = {q_strides, k_strides, v_strides, o_strides,
+                                     do_strides, dq_strides, dk_strides, dv_strides};
+    for (const int64_t *st : all_strides)
+        if (!strides_ok(st, 3, eb)) return SSA_ERR_INVALID_ARG;
+    if (batch == 0 || seq_len == 0) return SSA_OK;
+    const void *ptrs[10] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
+    for (int n = 0; n < 9; ++n)
+        if (!ptrs[n] || !aligned16(ptrs[n])) return SSA_ERR_INVALID_ARG;
+    if (!ssa::backward_supported(dtype == SSA_BF16, d_qk, d_v)) return SSA_ERR_UNSUPPORTED;
+    // Kernels index positions in int32 and address a 64-row tile with 32-bit
+    // byte offsets from its first row.
+    if (seq_len > kInt32Max - 256 || k_strides[1] >= (int64_t(1) << 24) ||
+        v_strides[1] >= (int64_t(1) << 24) || q_strides[1] >= (int64_t(1) << 24) ||
+        do_strides[1] >= (int64_t(1) << 24))
+        return SSA_ERR_UNSUPPORTED;
+    const BackwardPlan pl = backward_plan(batch, seq_len, heads_q, heads_kv, d_qk, d_v, pattern);
+    if (pl.dq_wgs >= (int64_t(1) << 24) || pl.dkv_wgs >= (int64_t(1) << 24) ||
+        pl.fin_wgs >= (int64_t(1) << 24) || pl.n_chunks * batch * heads_kv > kInt32Max)
+        return SSA_ERR_UNSUPPORTED;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < pl.total) return SSA_ERR_WORKSPACE;
+
+    ssa::BackwardArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = q_strides[i];
+        a.ks[i] = k_strides[i];
+        a.vs[i] = v_strides[i];
+        a.os[i] = o_strides[i];
+        a.dos[i] = do_strides[i];
+        a.dqs[i] = dq_strides[i];
+        a.dks[i] = dk_strides[i];
+        a.dvs[i] = dv_strides[i];
+    }
+    a.B = batch;
+    a.N = seq_len;
+    a.Hq = heads_q;
+    a.Hkv = heads_kv;
+    a.group = heads_q / heads_kv;
+    a.block = pattern.block;
+    a.sink = pattern.sink;
+    a.local = pattern.local;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.rowstat = static_cast<float *>(workspace);
+    a.sink_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.part_offset);
+    a.n_pad = (int32_t)pl.n_pad;
+    a.num_qtiles = (int32_t)pl.num_qtiles;
+    a.sink_tiles = (int32_t)pl.sink_tiles;
+    a.sink_rows = (int32_t)pl.sink_rows;
+    a.chunk_rows = (int32_t)pl.chunk_rows;
+    a.n_chunks = (int32_t)pl.n_chunks;
+    a.dq_wgs = (int32_t)pl.dq_wgs;
+    a.dkv_wgs = (int32_t)pl.dkv_wgs;
+    a.fin_wgs = (int32_t)pl.fin_wgs;
+    return ssa::launch_backward(dtype == SSA_BF16, d_qk, d_v, a, stream) == hipSuccess ? SSA_OK
+                                                                                       : SSA_ERR_HIP;
+}
+
+size_t ssa_prefill_backward_workspace_size(ssa_dtype dtype, int32_t batch, int32_t seq_len,
+                                           int32_t heads_q, int32_t heads_kv, int32_t d_qk,
+                                           int32_t d_v, ssa_pattern pattern) {
+    if (!backward_shape_ok(dtype, batch, seq_len, heads_q, heads_kv, d_qk, d_v, pattern)) return 0;
+    if (!ssa::backward_supported(dtype == SSA_BF16, d_qk, d_v)) return 0;
+    if (batch == 0 || seq_len == 0) return 0;
+    return backward_plan(batch, seq_len, heads_q, heads_kv, d_qk, d_v, pattern).total;
 }
 
 ssa_status ssa_decode(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,

@@ -1,0 +1,654 @@
+// Streaming sparse attention (SSA) backward for gfx950: dq, dk, dv.
+//
+// The gradient of the prefill operator (LongCat ZigZag Attention digest,
+// section 01 part (1): the SSA paragraph gives the operator, the training
+// paragraph and part (2) train the sparsified layers further). With
+// P_ij = exp(scale q_i.k_j - lse_i) on the attended pairs and
+// D_i = sum_d dO_id O_id (which equals sum_j P_ij dO_i.v_j):
+//   dS_ij = P_ij (dO_i.v_j - D_i)
+//   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+//   dv_j = sum_i P_ij dO_i.
+//
+// Three launches on the caller's stream:
+//  1. dq: one work-group per 128 query rows of one head, visiting the same key
+//     sub-tiles as the forward (the sink range and the local range, 64 keys
+//     at a time). It also stores each row's lse*log2(e) and D for launch 2.
+//  2. dk/dv: one work-group per 128 keys of one kv head, visiting the query
+//     rows that attend them, for every query head of the group. A key j past
+//     the sink is attended by rows [j, (j/b + l)*b), at most l*b of them. A
+//     sink key is attended by every later row, so the rows of a key tile that
+//     holds sink keys are cut into chunks, one work-group each, that write
+//     fp32 partial sums; the work stays balanced at any length.
+//  3. finalize: sums the sink partials in chunk order (deterministic) and
+//     writes bf16.
+//
+// Both MFMA kernels use the transposed form of the forward, in which one lane
+// owns one row of the tile (v_mfma_f32_32x32x16_bf16 accumulator layout):
+//  * dq: S^T = K Q^T and dP^T = V dO^T put one query per lane, so its lse and
+//    D are lane constants; dq^T += K^T dS^T takes dS^T straight from the
+//    score registers and reads K^T from LDS with transpose reads.
+//  * dk/dv: S = Q K^T and dP = dO V^T put one key per lane (K and V rows stay
+//    in registers); dv^T += dO^T P and dk^T += Q^T dS take P and dS from the
+//    registers and read dO^T and Q^T transposed.
+// Operand tiles are streamed global -> LDS by direct transfers into two
+// buffers (tile t+1 in flight while t is computed). Tiles read both row-wise
+// and transposed share one XOR swizzle that keeps both patterns free of bank
+// conflicts.
+#include "common.h"
+#include "kernels.h"
+#include "tiles.h"
+
+namespace ssa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 64;  // query rows per dk/dv sub-tile
+
+// Register budgets. dq holds q, dO (B operands) and the dq accumulators per
+// lane: two work-groups per CU fit up to d_qk = 128 with everything in VGPRs;
+// at d_qk = 192 one work-group per CU, with the operands parked in AGPRs.
+// dk/dv holds K, V (parked in AGPRs) and both accumulators: two work-groups
+// per CU only for d_qk + d_v < 256.
+template <int DQK>
+constexpr bool kParkDq = DQK > 128;
+template <int DQK>
+constexpr int kDqOccupancy = DQK > 128 ? 1 : 2;
+template <int DQK, int DV>
+constexpr int kDkvOccupancy = DQK + DV < 256 ? 2 : 1;
+
+// XOR swizzle, in 16-byte units, of row `row` of a bf16 tile with C units per
+// row. Two read patterns must hit distinct banks: 16 consecutive rows at one
+// unit (operand reads) and 4 consecutive rows x 4 consecutive units
+// (transpose reads).
+//  * Rows a multiple of 256 bytes: a bijection of the row's low 4 bits whose
+//    top two bits are row & 3.
+//  * Rows of 128 bytes mod 256 (d = 64, 192): consecutive rows already sit in
+//    opposite bank halves, so the swizzle (3 bits) separates rows of equal
+//    parity, and gives rows r and r + 2 different bit 2.
+// In both cases swz(r + 8) = swz(r) ^ 2 and swz(r + 16) = swz(r).
+template <int C>
+__device__ __forceinline__ int dual_swz(int row) {
+    if constexpr (C % 16 == 0) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Byte offset, from the tile's first row, of the 16 bytes that lane slot p of
+// a tile transfer fetches: tile row p / C at physical unit p % C, which holds
+// logical unit (p % C) ^ swz(row). Rows past rows_valid re-read the last valid
+// row; those rows are masked by the consumer.
+template <int C>
+__device__ __forceinline__ uint32_t dma_off(int p, int stride, int rows_valid) {
+    int row = p / C;
+    const int unit = (p % C) ^ dual_swz<C>(row);
+    row = row < rows_valid ? row : rows_valid - 1;
+    return (uint32_t)(row * stride + unit * 8) * 2u;
+}
+
+// Lane-constant LDS byte offsets of the two read patterns of a swizzled tile
+// with C units per row (row bytes 16 * C):
+//  * operand reads: lane (l32, hi) reads row l32 (+32 per block) at logical
+//    unit 2 ks + hi; since 2 ks and hi occupy different bits, the physical
+//    byte offset is (32 (ks & 7)) ^ z + 256 (ks >> 3) from the row, with
+//    z = (hi ^ swz(l32)) << 4;
+//  * transpose reads: lane s of 16-lane group G reads row 4 hi + s / 4 at
+//    column 16 (G & 1) + 4 (s & 3) of each 32-column block dd; the offset of
+//    the 8 rows below is (off ^ 32) + 8 rows, as swz(r + 8) = swz(r) ^ 2.
+template <int C>
+__device__ __forceinline__ uint32_t tr_lane_off(int lane, int dd) {
+    const int hi = lane >> 5, grp = lane >> 4, s16 = lane & 15;
+    const int row = 4 * hi + (s16 >> 2);
+    const int f = dual_swz<C>(row);
+    const int w = 2 * (grp & 1) + ((s16 & 3) >> 1);
+    return (uint32_t)row * (C * 16) + (uint32_t)((4 * (dd ^ (f >> 2)) + (w ^ (f & 3))) << 4) +
+           (uint32_t)((s16 & 1) << 3);
+}
+
+template <int C>
+__device__ __forceinline__ uint32_t operand_off(int ks, uint32_t z) {
+    return (((uint32_t)(32 * (ks & 7))) ^ z) + (uint32_t)(ks >> 3) * 256u;
+}
+
+// 32x32x16 A operand of 16 tile rows from two transpose reads: rows
+// blk + 4 hi + {0..3} and blk + 8 + 4 hi + {0..3}, one column per lane.
+template <int C>
+__device__ __forceinline__ bf16x8 tr_operand(const char *tile, uint32_t lane_off, uint32_t blk_bytes) {
+    const i16x4 lo = lds_read_tr16(tile + lane_off + blk_bytes);
+    const i16x4 up = lds_read_tr16(tile + ((lane_off ^ 32u) + blk_bytes + 8u * (C * 16)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float *x) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// Write a 32x32 transposed accumulator block (rows = 32 columns of an output
+// row, lane = the row) times `mul` as bf16: lane (l32, hi) owns columns
+// 8 rq + 4 hi + {0..3} of block dd.
+__device__ __forceinline__ void store_row_block(uint16_t *row, const f32x16 &acc, int dd, int hi, float mul) {
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+        const int col = dd * 32 + 8 * rq + 4 * hi;
+        *(u32x2 *)(row + col) = u32x2{pack_bf16x2(acc[4 * rq] * mul, acc[4 * rq + 1] * mul),
+                                      pack_bf16x2(acc[4 * rq + 2] * mul, acc[4 * rq + 3] * mul)};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch 1: dq (+ per-row lse * log2 e and D).
+// ---------------------------------------------------------------------------
+template <int DQK, int DV>
+__global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(const BackwardArgs a) {
+    constexpr int CK = DQK / 8, CV = DV / 8;   // 16-byte units per K / V row
+    constexpr int NIK = CK / 4, NIV = CV / 4;  // transfers per wave per sub-tile
+    constexpr int NDMA = NIK + NIV;
+    constexpr int NQ = DQK / 16, NV = DV / 16, NDQ = DQK / 32;
+    constexpr uint32_t RBK = DQK * 2, RBV = DV * 2;
+    static_assert(CK % 4 == 0 && CV % 4 == 0, "tile rows must split into whole waves");
+    constexpr uint32_t KBUF = kBN * DQK * 2, VBUF = kBN * DV * 2;  // bytes per buffer
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][kBN * DQK];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][kBN * DV];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    const int wg = xcd_remap(blockIdx.x, a.dq_wgs);
+    const int qt = wg % a.num_qtiles;
+    const int hb = wg / a.num_qtiles;
+    const int h = hb % a.Hq, bb = hb / a.Hq;
+    const int g = h / a.group;
+
+    const TileRanges tr = tile_ranges(a, qt);
+    const int i = tr.q0 + wave * 32 + l32;  // this lane's query row
+    const bool row_ok = i < a.N;
+    const int lo_i = local_start(a, i);
+
+    // q and dO of row i as B operands (lane half hi holds 8 of each 16
+    // columns), lse in log2 units, and D = dO . O over the whole row.
+    bf16x8 qf[NQ], df[NV];
+    float lse2 = 0.f, dsum = 0.f;
+    {
+        const int64_t ii = row_ok ? i : 0;
+        const uint16_t *qrow = (const uint16_t *)a.q + bb * a.qs[0] + ii * a.qs[1] + h * a.qs[2] + 8 * hi;
+        const uint16_t *drow = (const uint16_t *)a.dout + bb * a.dos[0] + ii * a.dos[1] + h * a.dos[2] + 8 * hi;
+        const uint16_t *orow = (const uint16_t *)a.o + bb * a.os[0] + ii * a.os[1] + h * a.os[2] + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < NQ; ++ks) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (row_ok) w = *(const u32x4 *)(qrow + ks * 16);
+            qf[ks] = __builtin_bit_cast(bf16x8, w);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NV; ++ks) {
+            u32x4 dw = {0u, 0u, 0u, 0u}, ow = {0u, 0u, 0u, 0u};
+            if (row_ok) {
+                dw = *(const u32x4 *)(drow + ks * 16);
+                ow = *(const u32x4 *)(orow + ks * 16);
+            }
+            df[ks] = __builtin_bit_cast(bf16x8, dw);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dsum += bf16_lo(dw[e]) * bf16_lo(ow[e]) + bf16_hi(dw[e]) * bf16_hi(ow[e]);
+        }
+        if (row_ok) lse2 = a.lse[((int64_t)bb * a.Hq + h) * a.N + i] * kLog2e;
+        if constexpr (kParkDq<DQK>) {
+            // Read-only MFMA operands live in AGPRs for the whole tile; the
+            // VGPRs hold the accumulators, whose scores feed VALU work.
+#pragma unroll
+            for (int ks = 0; ks < NQ; ++ks) asm volatile("" : "+a"(qf[ks]));
+#pragma unroll
+            for (int ks = 0; ks < NV; ++ks) asm volatile("" : "+a"(df[ks]));
+        }
+    }
+    dsum += __shfl_xor(dsum, 32);
+    if (hi == 0) {
+        // Rows N..n_pad-1 of the last tile store zeros (finite, never used).
+        float *rs = a.rowstat + (((int64_t)bb * a.Hq + h) * (a.n_pad >> 6) + (i >> 6)) * 128 + (i & 63);
+        rs[0] = lse2;
+        rs[64] = dsum;
+    }
+
+    const uint16_t *kbase = (const uint16_t *)a.k + bb * a.ks[0] + g * a.ks[2];
+    const uint16_t *vbase = (const uint16_t *)a.v + bb * a.vs[0] + g * a.vs[2];
+    const int ks1 = (int)a.ks[1], vs1 = (int)a.vs[1];  // token strides (< 2^24, host-checked)
+
+    const uint32_t k_lds0 = lds_addr(&k_lds[0][0]), v_lds0 = lds_addr(&v_lds[0][0]);
+    auto issue = [&](int t) {
+        const SubTile st = sub_tile(tr, t);
+        const int rows_valid = st.re - st.j0;
+        const char *kt = (const char *)(kbase + (int64_t)st.j0 * a.ks[1]);
+        const char *vt = (const char *)(vbase + (int64_t)st.j0 * a.vs[1]);
+        const uint32_t kb = __builtin_amdgcn_readfirstlane(k_lds0 + (t & 1) * KBUF);
+        const uint32_t vb = __builtin_amdgcn_readfirstlane(v_lds0 + (t & 1) * VBUF);
+#pragma unroll
+        for (int n = 0; n < NIK; ++n) {
+            const int p = (wave * NIK + n) * 64 + lane;
+            dma16_untracked(kt + dma_off<CK>(p, ks1, rows_valid), kb + (wave * NIK + n) * 1024);
+        }
+#pragma unroll
+        for (int n = 0; n < NIV; ++n) {
+            const int p = (wave * NIV + n) * 64 + lane;
+            dma16_untracked(vt + dma_off<CV>(p, vs1, rows_valid), vb + (wave * NIV + n) * 1024);
+        }
+    };
+
+    f32x16 dqacc[NDQ];
+#pragma unroll
+    for (int d = 0; d < NDQ; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqacc[d][r] = 0.f;
+
+    const uint32_t k_row = (uint32_t)l32 * RBK, kz = (uint32_t)((hi ^ dual_swz<CK>(l32)) << 4);
+    const uint32_t v_row = (uint32_t)l32 * RBV, vz = (uint32_t)((hi ^ dual_swz<CV>(l32)) << 4);
+    const int jl = 4 * hi;  // key offset of this lane's accumulator rows
+
+    const int r_first = tr.q0 + wave * 32;
+    const int r_last = r_first + 31 < a.N - 1 ? r_first + 31 : a.N - 1;
+    const int lo_first_w = local_start(a, r_first), lo_last_w = local_start(a, r_last);
+
+    auto compute = [&](int t) {
+        const uint16_t *kb = k_lds[t & 1];
+        const uint16_t *vb = v_lds[t & 1];
+        const SubTile st = sub_tile(tr, t);
+        const bool local = t >= tr.n_sink;
+        const int kend = st.j0 + kBN < st.re ? st.j0 + kBN : st.re;
+        if (r_first >= a.N || st.j0 > r_last || (local && kend <= lo_first_w)) return;
+        const bool full = st.j0 + kBN <= st.re && (!local || st.j0 >= lo_last_w);
+        const bool no_mask = full && st.j0 + kBN - 1 <= r_first;
+        const bool causal_only = full && !no_mask;
+        // Re-derive the lane offsets here (the empty asm hides their origin)
+        // so that address arithmetic is not hoisted out of the pipelined loop
+        // into registers that would stay live across it.
+        uint32_t k_off = k_row, kzz = kz, v_off = v_row, vzz = vz, lane_r = (uint32_t)lane;
+        asm volatile("" : "+v"(k_off), "+v"(kzz), "+v"(v_off), "+v"(vzz), "+v"(lane_r));
+        const char *kc = (const char *)kb;
+        const char *vc = (const char *)vb;
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk) {
+            if (st.j0 + 32 * kbk > r_last) break;  // the wave's rows precede these keys
+            f32x16 sacc, pacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+            const char *krow = kc + k_off + kbk * 32 * RBK;
+            const char *vrow = vc + v_off + kbk * 32 * RBV;
+#pragma unroll
+            for (int ks = 0; ks < NQ; ++ks) {
+                const bf16x8 kf = *(const bf16x8 *)(krow + operand_off<CK>(ks, kzz));
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int ks = 0; ks < NV; ++ks) {
+                const bf16x8 vf = *(const bf16x8 *)(vrow + operand_off<CV>(ks, vzz));
+                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[ks], pacc, 0, 0, 0);
+            }
+            // dS^T: accumulator element r is key kbk*32 + 8(r/4) + 4hi + r%4.
+            float ds[16];
+            const int d0 = i - (st.j0 + jl + 32 * kbk);
+            const int jb = st.j0 + jl + 32 * kbk;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = 8 * (r >> 2) + (r & 3);
+                float p = fast_exp2(__builtin_fmaf(sacc[r], a.scale_log2, -lse2));
+                if (causal_only) {
+                    p = kk <= d0 ? p : 0.f;
+                } else if (!no_mask) {
+                    const int j = jb + kk;
+                    const bool ok = (j < st.re) & (j <= i) & ((j < tr.sb) | (j >= lo_i));
+                    p = ok ? p : 0.f;
+                }
+                ds[r] = p * (pacc[r] - dsum);
+            }
+            // dq^T += K^T dS^T. Instruction c consumes keys 16c + {0..3, 8..11}
+            // (+4 on the upper half-wave): accumulator elements 8c..8c+7.
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const bf16x8 sf = pack8(ds + 8 * c);
+                const uint32_t blk = (uint32_t)(kbk * 32 + 16 * c) * RBK;
+#pragma unroll
+                for (int dd = 0; dd < NDQ; ++dd)
+                    dqacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CK>(kc, tr_lane_off<CK>((int)lane_r, dd), blk),
+                                                                        sf, dqacc[dd], 0, 0, 0);
+            }
+        }
+    };
+
+    // Two-buffer ring: sub-tile t+1 streams in while t is computed. The
+    // transfers are invisible to the compiler, so the explicit wait (all but
+    // the newest sub-tile's transfers done) and the barriers alone order the
+    // buffers.
+    const int T = tr.n_total;
+    if (T > 0) issue(0);
+    for (int t = 0; t < T; ++t) {
+        if (t + 1 < T) {
+            issue(t + 1);
+            wait_vmcnt<NDMA>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        barrier_no_fence();
+        compute(t);
+        barrier_lds_drained();
+    }
+
+    if (row_ok) {
+        uint16_t *dqrow = (uint16_t *)a.dq + bb * a.dqs[0] + (int64_t)i * a.dqs[1] + h * a.dqs[2];
+#pragma unroll
+        for (int dd = 0; dd < NDQ; ++dd) store_row_block(dqrow, dqacc[dd], dd, hi, a.scale);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch 2: dk, dv.
+// ---------------------------------------------------------------------------
+// Last query row (exclusive) that attends key j: every row for a sink key,
+// else the end of the l-th block from j's own block; clamped to N.
+__device__ __forceinline__ int key_row_end(const BackwardArgs &a, int j) {
+    const int64_t sb = (int64_t)a.sink * a.block;
+    if (j < sb) return a.N;
+    const int64_t e = ((int64_t)(j / a.block) + a.local) * a.block;
+    return (int)(e < a.N ? e : a.N);
+}
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(kThreads, (kDkvOccupancy<DQK, DV>)) void ssa_bwd_dkv_bf16(const BackwardArgs a) {
+    constexpr int CQ = DQK / 8, CD = DV / 8;   // 16-byte units per q / dO row
+    constexpr int NIQ = CQ / 4, NID = CD / 4;  // transfers per wave per sub-tile
+    constexpr int NDMA = NIQ + NID + 1;        // + the row statistics
+    constexpr int NQ = DQK / 16, NV = DV / 16, NDK = DQK / 32, NDV = DV / 32;
+    constexpr uint32_t RBQ = DQK * 2, RBD = DV * 2;
+    static_assert(CQ % 4 == 0 && CD % 4 == 0, "tile rows must split into whole waves");
+    constexpr uint32_t QBUF = kRows * DQK * 2, DBUF = kRows * DV * 2;  // bytes per buffer
+    __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][kRows * DQK];
+    __shared__ __attribute__((aligned(1024))) uint16_t d_lds[2][kRows * DV];
+    __shared__ __attribute__((aligned(16))) float s_lds[2][128];  // lse * log2 e [64], D [64]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    // Work-groups [0, n_part): (chunk, sink key tile, kv head, batch); the
+    // rest: (key tile past the sink tiles, kv head, batch).
+    const int wg = xcd_remap(blockIdx.x, a.dkv_wgs);
+    const int n_part = a.sink_tiles * a.n_chunks * a.Hkv * a.B;
+    const bool part = wg < n_part;
+    int kt, g, bb, ch = 0, r0, r1;
+    if (part) {
+        int x = wg;
+        ch = x % a.n_chunks;
+        x /= a.n_chunks;
+        kt = x % a.sink_tiles;
+        x /= a.sink_tiles;
+        g = x % a.Hkv;
+        bb = x / a.Hkv;
+        const int c0 = ch * a.chunk_rows;
+        r0 = kt * kBM > c0 ? kt * kBM : c0;
+        const int64_t c1 = (int64_t)c0 + a.chunk_rows;
+        r1 = c1 < a.N ? (int)c1 : a.N;
+    } else {
+        int x = wg - n_part;
+        const int nt = a.num_qtiles - a.sink_tiles;
+        kt = a.sink_tiles + x % nt;
+        x /= nt;
+        g = x % a.Hkv;
+        bb = x / a.Hkv;
+        const int k1 = kt * kBM + kBM < a.N ? kt * kBM + kBM : a.N;
+        r0 = kt * kBM;
+        r1 = key_row_end(a, k1 - 1);
+    }
+    const int nsub = r1 > r0 ? (r1 - r0 + kRows - 1) / kRows : 0;
+    const int T = a.group * nsub;
+
+    // This lane's key: its K and V rows as B operands, and the rows that
+    // attend it within this work-group's range: [j, up_j).
+    const int j = kt * kBM + wave * 32 + l32;
+    const bool key_ok = j < a.N;
+    const int re_j = key_row_end(a, key_ok ? j : a.N - 1);
+    const int up_j = re_j < r1 ? re_j : r1;
+    bf16x8 kf[NQ], vf[NV];
+    {
+        const int64_t jj = key_ok ? j : 0;
+        const uint16_t *krow = (const uint16_t *)a.k + bb * a.ks[0] + jj * a.ks[1] + g * a.ks[2] + 8 * hi;
+        const uint16_t *vrow = (const uint16_t *)a.v + bb * a.vs[0] + jj * a.vs[1] + g * a.vs[2] + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < NQ; ++ks) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (key_ok) w = *(const u32x4 *)(krow + ks * 16);
+            kf[ks] = __builtin_bit_cast(bf16x8, w);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NV; ++ks) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (key_ok) w = *(const u32x4 *)(vrow + ks * 16);
+            vf[ks] = __builtin_bit_cast(bf16x8, w);
+        }
+        if constexpr (kDkvOccupancy<DQK, DV> == 1) {
+            // Read-only MFMA operands live in AGPRs for the whole work-group.
+#pragma unroll
+            for (int ks = 0; ks < NQ; ++ks) asm volatile("" : "+a"(kf[ks]));
+#pragma unroll
+            for (int ks = 0; ks < NV; ++ks) asm volatile("" : "+a"(vf[ks]));
+        }
+    }
+    // Wave-uniform bounds: first and last valid key of the wave, and the
+    // least and greatest row end over its keys. Sink keys are attended up to
+    // r1; past the sink, row ends grow with j.
+    const int jw_first = kt * kBM + wave * 32;
+    const int jw_last = jw_first + 31 < a.N - 1 ? jw_first + 31 : a.N - 1;
+    const bool wave_live = jw_first < a.N;
+    const int64_t sb = (int64_t)a.sink * a.block;
+    int up_min = 0, up_max = 0;
+    if (wave_live) {
+        const int e_last = key_row_end(a, jw_last) < r1 ? key_row_end(a, jw_last) : r1;
+        const int j_past = jw_first >= sb ? jw_first : (sb < jw_last ? (int)sb : jw_last);  // first key past the sink
+        const int e_past = key_row_end(a, j_past) < r1 ? key_row_end(a, j_past) : r1;
+        up_max = jw_first < sb ? r1 : e_last;
+        up_min = jw_last < sb ? r1 : e_past;
+    }
+
+    const int64_t qs1 = a.qs[1], ds1 = a.dos[1];
+    const int qs1i = (int)qs1, ds1i = (int)ds1;  // token strides (< 2^24, host-checked)
+    const int64_t rs_groups = a.n_pad >> 6;
+
+    const uint32_t q_lds0 = lds_addr(&q_lds[0][0]), d_lds0 = lds_addr(&d_lds[0][0]);
+    const uint32_t s_lds0 = lds_addr(&s_lds[0][0]);
+    auto issue = [&](int t) {
+        const uint32_t qb = __builtin_amdgcn_readfirstlane(q_lds0 + (t & 1) * QBUF);
+        const uint32_t db = __builtin_amdgcn_readfirstlane(d_lds0 + (t & 1) * DBUF);
+        const uint32_t sb = s_lds0 + (t & 1) * 512u;
+        const int hh = g * a.group + t / nsub;
+        const int i0 = r0 + kRows * (t % nsub);
+        const int rows_valid = r1 - i0 < kRows ? r1 - i0 : kRows;
+        const char *qt = (const char *)((const uint16_t *)a.q + bb * a.qs[0] + (int64_t)i0 * qs1 + hh * a.qs[2]);
+        const char *dt = (const char *)((const uint16_t *)a.dout + bb * a.dos[0] + (int64_t)i0 * ds1 + hh * a.dos[2]);
+#pragma unroll
+        for (int n = 0; n < NIQ; ++n) {
+            const int p = (wave * NIQ + n) * 64 + lane;
+            dma16_untracked(qt + dma_off<CQ>(p, qs1i, rows_valid), qb + (wave * NIQ + n) * 1024);
+        }
+#pragma unroll
+        for (int n = 0; n < NID; ++n) {
+            const int p = (wave * NID + n) * 64 + lane;
+            dma16_untracked(dt + dma_off<CD>(p, ds1i, rows_valid), db + (wave * NID + n) * 1024);
+        }
+        // Row statistics of rows i0..i0+63 (512 contiguous bytes): 128 per wave.
+        const float *src = a.rowstat + (((int64_t)bb * a.Hq + hh) * rs_groups + (i0 >> 6)) * 128 + wave * 32 + 4 * lane;
+        const uint32_t s_dst = __builtin_amdgcn_readfirstlane(sb + wave * 128);
+        if (lane < 8) dma16_untracked(src, s_dst);
+    };
+
+    f32x16 dkacc[NDK], dvacc[NDV];
+#pragma unroll
+    for (int d = 0; d < NDK; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dkacc[d][r] = 0.f;
+#pragma unroll
+    for (int d = 0; d < NDV; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dvacc[d][r] = 0.f;
+
+    const uint32_t q_row = (uint32_t)l32 * RBQ, qz = (uint32_t)((hi ^ dual_swz<CQ>(l32)) << 4);
+    const uint32_t d_row = (uint32_t)l32 * RBD, dz = (uint32_t)((hi ^ dual_swz<CD>(l32)) << 4);
+
+    auto compute = [&](int t) {
+        if (!wave_live) return;
+        const uint16_t *qb = q_lds[t & 1];
+        const uint16_t *db = d_lds[t & 1];
+        const float *sb = s_lds[t & 1];
+        const int i0 = r0 + kRows * (t % nsub);
+        uint32_t q_off = q_row, qzz = qz, d_off = d_row, dzz = dz, lane_r = (uint32_t)lane;
+        asm volatile("" : "+v"(q_off), "+v"(qzz), "+v"(d_off), "+v"(dzz), "+v"(lane_r));
+        const char *qc = (const char *)qb;
+        const char *dc = (const char *)db;
+#pragma unroll
+        for (int qblk = 0; qblk < 2; ++qblk) {
+            const int ib = i0 + 32 * qblk;  // first row of the block
+            if (ib + 31 < jw_first || ib >= up_max) continue;  // no pair of the wave is attended
+            const bool no_mask = ib >= jw_last && ib + 31 < up_min;
+            f32x16 sacc, pacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+            const char *qrow = qc + q_off + qblk * 32 * RBQ;
+            const char *drow = dc + d_off + qblk * 32 * RBD;
+#pragma unroll
+            for (int ks = 0; ks < NQ; ++ks) {
+                const bf16x8 qa = *(const bf16x8 *)(qrow + operand_off<CQ>(ks, qzz));
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sacc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int ks = 0; ks < NV; ++ks) {
+                const bf16x8 da = *(const bf16x8 *)(drow + operand_off<CD>(ks, dzz));
+                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], pacc, 0, 0, 0);
+            }
+            // Accumulator element r is row ib + 8(r/4) + 4hi + r%4.
+            float pv[16], ds[16];
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int rl = 32 * qblk + 8 * rq + 4 * hi;  // row within the sub-tile
+                const f32x4 l4 = *(const f32x4 *)(sb + rl);
+                const f32x4 d4 = *(const f32x4 *)(sb + 64 + rl);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * rq + e;
+                    float p = fast_exp2(__builtin_fmaf(sacc[r], a.scale_log2, -l4[e]));
+                    if (!no_mask) {
+                        const int row = ib + 8 * rq + 4 * hi + e;
+                        p = ((row >= j) & (row < up_j)) ? p : 0.f;
+                    }
+                    pv[r] = p;
+                    ds[r] = p * (pacc[r] - d4[e]);
+                }
+            }
+            // dv^T += dO^T P and dk^T += Q^T dS. Instruction c consumes rows
+            // 16c + {0..3, 8..11} (+4 on the upper half-wave): accumulator
+            // elements 8c..8c+7.
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const bf16x8 pf = pack8(pv + 8 * c);
+                const bf16x8 sf = pack8(ds + 8 * c);
+                const uint32_t blkq = (uint32_t)(qblk * 32 + 16 * c) * RBQ;
+                const uint32_t blkd = (uint32_t)(qblk * 32 + 16 * c) * RBD;
+#pragma unroll
+                for (int dd = 0; dd < NDV; ++dd)
+                    dvacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CD>(dc, tr_lane_off<CD>((int)lane_r, dd), blkd),
+                                                                        pf, dvacc[dd], 0, 0, 0);
+#pragma unroll
+                for (int dd = 0; dd < NDK; ++dd)
+                    dkacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CQ>(qc, tr_lane_off<CQ>((int)lane_r, dd), blkq),
+                                                                        sf, dkacc[dd], 0, 0, 0);
+            }
+        }
+    };
+
+    if (T > 0) issue(0);
+    for (int t = 0; t < T; ++t) {
+        if (t + 1 < T) {
+            issue(t + 1);
+            wait_vmcnt<NDMA>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        barrier_no_fence();
+        compute(t);
+        barrier_lds_drained();
+    }
+
+    if (!key_ok) return;
+    if (!part) {
+        uint16_t *dkrow = (uint16_t *)a.dk + bb * a.dks[0] + (int64_t)j * a.dks[1] + g * a.dks[2];
+        uint16_t *dvrow = (uint16_t *)a.dv + bb * a.dvs[0] + (int64_t)j * a.dvs[1] + g * a.dvs[2];
+#pragma unroll
+        for (int dd = 0; dd < NDK; ++dd) store_row_block(dkrow, dkacc[dd], dd, hi, a.scale);
+#pragma unroll
+        for (int dd = 0; dd < NDV; ++dd) store_row_block(dvrow, dvacc[dd], dd, hi, 1.f);
+    } else {
+        float *dst = a.sink_part + ((((int64_t)ch * a.B + bb) * a.Hkv + g) * a.sink_rows + j) * (DQK + DV);
+#pragma unroll
+        for (int dd = 0; dd < NDK; ++dd)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq)
+                *(f32x4 *)(dst + dd * 32 + 8 * rq + 4 * hi) =
+                    f32x4{dkacc[dd][4 * rq] * a.scale, dkacc[dd][4 * rq + 1] * a.scale,
+                          dkacc[dd][4 * rq + 2] * a.scale, dkacc[dd][4 * rq + 3] * a.scale};
+#pragma unroll
+        for (int dd = 0; dd < NDV; ++dd)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq)
+                *(f32x4 *)(dst + DQK + dd * 32 + 8 * rq + 4 * hi) =
+                    f32x4{dvacc[dd][4 * rq], dvacc[dd][4 * rq + 1], dvacc[dd][4 * rq + 2], dvacc[dd][4 * rq + 3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch 3: sum the sink partials over the chunks, in chunk order.
+// ---------------------------------------------------------------------------
+template <int DQK, int DV>
+__global__ __launch_bounds__(kThreads) void ssa_bwd_sink_finalize(const BackwardArgs a) {
+    constexpr int W = (DQK + DV) / 4;  // 4-column groups per row
+    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t rows = (int64_t)a.B * a.Hkv * a.sink_rows;
+    if (idx >= rows * W) return;
+    const int c = 4 * (int)(idx % W);
+    const int64_t row = idx / W;  // (batch, kv head, key)
+    const int j = (int)(row % a.sink_rows);
+    const int g = (int)((row / a.sink_rows) % a.Hkv);
+    const int bb = (int)(row / ((int64_t)a.sink_rows * a.Hkv));
+    const float *src = a.sink_part + row * (DQK + DV) + c;
+    const int64_t slice = rows * (DQK + DV);
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < a.n_chunks; ++k) s += *(const f32x4 *)(src + k * slice);
+    uint16_t *dst = c < DQK ? (uint16_t *)a.dk + bb * a.dks[0] + (int64_t)j * a.dks[1] + g * a.dks[2] + c
+                            : (uint16_t *)a.dv + bb * a.dvs[0] + (int64_t)j * a.dvs[1] + g * a.dvs[2] + (c - DQK);
+    *(u32x2 *)dst = u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+}
+
+template <int DQK, int DV>
+hipError_t launch_all(const BackwardArgs &a, hipStream_t stream) {
+    void *args[] = {(void *)&a};
+    hipError_t e = hipLaunchKernel((const void *)ssa_bwd_dq_bf16<DQK, DV>, dim3(a.dq_wgs), dim3(kThreads), args, 0,
+                                   stream);
+    if (e != hipSuccess) return e;
+    e = hipLaunchKernel((const void *)ssa_bwd_dkv_bf16<DQK, DV>, dim3(a.dkv_wgs), dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess || a.fin_wgs == 0) return e;
+    return hipLaunchKernel((const void *)ssa_bwd_sink_finalize<DQK, DV>, dim3(a.fin_wgs), dim3(kThreads), args, 0,
+                           stream);
+}
+
+}  // namespace
+
+bool backward_supported(bool bf16, int d_qk, int d_v) {
+    return bf16 && ((d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128));
+}
+
+hipError_t launch_backward(bool bf16, int d_qk, int d_v, const BackwardArgs &a, hipStream_t stream) {
+    if (bf16) {
+        if (d_qk == 64 && d_v == 64) return launch_all<64, 64>(a, stream);
+        if (d_qk == 128 && d_v == 128) return launch_all<128, 128>(a, stream);
+        if (d_qk == 192 && d_v == 128) return launch_all<192, 128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ssa

@@ -21,6 +21,31 @@ struct PrefillArgs {
 bool prefill_supported(bool bf16, int d_qk, int d_v);
 hipError_t launch_prefill(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream);
 
+// Backward of the prefill operator. Workspace: per (batch, query head, group
+// of 64 rows) the rows' lse * log2(e) then their D = sum_d dO*O (128 floats),
+// and, for key tiles that hold sink keys, fp32 partial sums of dk (scaled)
+// and dv per chunk of query rows.
+struct BackwardArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;                    // [B, Hq, N], natural log, from the forward
+    void *dq, *dk, *dv;
+    int64_t qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];  // (batch, token, head)
+    int32_t B, N, Hq, Hkv, group;
+    int32_t block, sink, local;
+    float scale, scale_log2;
+    float *rowstat;                      // [B, Hq, n_pad / 64, 2, 64]
+    float *sink_part;                    // [n_chunks, B, Hkv, sink_rows, d_qk + d_v]
+    int32_t n_pad;                       // N rounded up to a multiple of 128
+    int32_t num_qtiles;                  // ceil(N / 128): query tiles, also key tiles
+    int32_t sink_tiles;                  // key tiles holding a sink key
+    int32_t sink_rows;                   // sink_tiles * 128, clamped to N
+    int32_t chunk_rows, n_chunks;        // query rows per sink chunk (multiple of 128)
+    int32_t dq_wgs, dkv_wgs, fin_wgs;    // grid sizes of the three launches
+};
+
+bool backward_supported(bool bf16, int d_qk, int d_v);
+hipError_t launch_backward(bool bf16, int d_qk, int d_v, const BackwardArgs &a, hipStream_t stream);
+
 enum DecodeKind { kDecodeValu = 0, kDecodeLatent = 1 };
 
 // The latent kernel keeps the page ids of one split in LDS. A split of T

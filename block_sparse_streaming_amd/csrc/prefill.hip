@@ -32,62 +32,15 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "tiles.h"
 
 namespace ssa {
 namespace {
 
-constexpr int kBM = 128;      // query rows per work-group
-constexpr int kBN = 64;       // keys per sub-tile
 constexpr int kThreads = 256;
 // Growth of a row max (log2 units) tolerated before the accumulators are
 // rescaled; probabilities stay below 2^8, far from fp32/bf16 overflow.
 constexpr float kRescaleSlack = 8.f;
-
-// Shared geometry of a query tile: its two key ranges and mask bounds. All
-// positions fit in int32 (seq_len is an int32); bounds are clamped to [0, N].
-struct TileRanges {
-    int q0, q1, sb, sink_end, loc_begin, lo_last;
-    int n_sink, n_total;  // sub-tiles in the sink range, in both ranges
-};
-
-// First key of the local window of query position q (block rule), in [0, N].
-__device__ __forceinline__ int local_start(const PrefillArgs &a, int64_t q) {
-    const int64_t lo = (q / a.block - a.local + 1) * (int64_t)a.block;
-    return (int)(lo < 0 ? 0 : (lo > a.N ? a.N : lo));
-}
-
-__device__ __forceinline__ TileRanges tile_ranges(const PrefillArgs &a, int qt) {
-    TileRanges r;
-    const int N = a.N;
-    const int64_t sb = (int64_t)a.sink * a.block;
-    r.sb = (int)(sb < N ? sb : N);
-    r.q0 = qt * kBM;
-    r.q1 = r.q0 + kBM < N ? r.q0 + kBM : N;
-    const int lo_first = local_start(a, r.q0);
-    r.lo_last = local_start(a, r.q1 - 1);
-    r.sink_end = r.sb < r.q1 ? r.sb : r.q1;
-    r.loc_begin = lo_first > r.sink_end ? lo_first : r.sink_end;
-    r.n_sink = (r.sink_end + kBN - 1) / kBN;
-    r.n_total = r.n_sink + (r.q1 - r.loc_begin + kBN - 1) / kBN;
-    return r;
-}
-
-// Sub-tile t of a tile: first key, end of its range, and whether any pair in
-// it can be masked (it crosses a range end, the diagonal of the tile's first
-// row or, in the local range, the window start of the tile's last row).
-struct SubTile {
-    int j0, re;
-    bool need_mask;
-};
-
-__device__ __forceinline__ SubTile sub_tile(const TileRanges &r, int t) {
-    SubTile s;
-    const bool local = t >= r.n_sink;
-    s.j0 = local ? r.loc_begin + (t - r.n_sink) * kBN : t * kBN;
-    s.re = local ? r.q1 : r.sink_end;
-    s.need_mask = !((s.j0 + kBN <= s.re) && (s.j0 + kBN - 1 <= r.q0) && (!local || s.j0 >= r.lo_last));
-    return s;
-}
 
 // ---------------------------------------------------------------------------
 // bf16: pipelined direct-to-LDS kernel.

@@ -1,0 +1,68 @@
+// Key ranges of a 128-row query tile under the SSA rule, shared by the
+// forward and the backward kernels.
+//
+// For query position i (block i / b), the attended keys are the sink range
+// [0, min(s*b, i+1)) and the local range [max(s*b, (i/b - l + 1)*b), i+1):
+// the first s blocks plus the l blocks ending at the query's own block,
+// causal (LongCat ZigZag Attention digest, section 01 part (1), the SSA
+// paragraph). Over a tile of rows [q0, q1) the union of the rows' key sets is
+// still two ranges, walked in 64-key sub-tiles.
+#pragma once
+
+#include <stdint.h>
+
+namespace ssa {
+
+constexpr int kBM = 128;  // query rows per work-group
+constexpr int kBN = 64;   // keys per sub-tile
+
+// First key of the local window of query position q, clamped to [0, N].
+// Args is any argument block with fields N, block, local.
+template <class Args>
+__device__ __forceinline__ int local_start(const Args &a, int64_t q) {
+    const int64_t lo = (q / a.block - a.local + 1) * (int64_t)a.block;
+    return (int)(lo < 0 ? 0 : (lo > a.N ? a.N : lo));
+}
+
+// A query tile's two key ranges and mask bounds. All positions fit in int32
+// (the sequence length is an int32); bounds are clamped to [0, N].
+struct TileRanges {
+    int q0, q1, sb, sink_end, loc_begin, lo_last;
+    int n_sink, n_total;  // sub-tiles in the sink range, in both ranges
+};
+
+template <class Args>
+__device__ __forceinline__ TileRanges tile_ranges(const Args &a, int qt) {
+    TileRanges r;
+    const int N = a.N;
+    const int64_t sb = (int64_t)a.sink * a.block;
+    r.sb = (int)(sb < N ? sb : N);
+    r.q0 = qt * kBM;
+    r.q1 = r.q0 + kBM < N ? r.q0 + kBM : N;
+    const int lo_first = local_start(a, r.q0);
+    r.lo_last = local_start(a, r.q1 - 1);
+    r.sink_end = r.sb < r.q1 ? r.sb : r.q1;
+    r.loc_begin = lo_first > r.sink_end ? lo_first : r.sink_end;
+    r.n_sink = (r.sink_end + kBN - 1) / kBN;
+    r.n_total = r.n_sink + (r.q1 - r.loc_begin + kBN - 1) / kBN;
+    return r;
+}
+
+// Sub-tile t of a tile: first key, end of its range, and whether any pair in
+// it can be masked (it crosses a range end, the diagonal of the tile's first
+// row or, in the local range, the window start of the tile's last row).
+struct SubTile {
+    int j0, re;
+    bool need_mask;
+};
+
+__device__ __forceinline__ SubTile sub_tile(const TileRanges &r, int t) {
+    SubTile s;
+    const bool local = t >= r.n_sink;
+    s.j0 = local ? r.loc_begin + (t - r.n_sink) * kBN : t * kBN;
+    s.re = local ? r.q1 : r.sink_end;
+    s.need_mask = !((s.j0 + kBN <= s.re) && (s.j0 + kBN - 1 <= r.q0) && (!local || s.j0 >= r.lo_last));
+    return s;
+}
+
+}  // namespace ssa

@@ -154,3 +154,9 @@ def decode_inputs(cfg: DecodeConfig, device, *, lens=None, seed: int | None = No
         v_cache = randn((num_pages, page_size, cfg.Hkv, cfg.d_v), cfg.dtype, device, gen)
     return DecodeInputs(q, k_cache, v_cache, torch.from_numpy(table).to(device),
                         torch.tensor(lens, dtype=torch.int32, device=device), table, lens)
+
+
+def prefill_grad(cfg: PrefillConfig, device, seed: int | None = None):
+    """Upstream gradient dout [B, N, Hq, d_v] for the backward of a prefill workload."""
+    gen = generator(device, cfg.seed + 50 if seed is None else seed)
+    return randn((cfg.B, cfg.N, cfg.Hq, cfg.d_v), cfg.dtype, device, gen)

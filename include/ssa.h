@@ -95,6 +95,56 @@ ssa_status ssa_prefill(ssa_dtype dtype, const void *q, const void *k, const void
                        hipStream_t stream);
 
 /*
+ * ssa_prefill_backward - gradients of ssa_prefill (same operator, same
+ * pattern). The digest trains the sparsified layers further after replacing
+ * them with SSA (section 01, part (1): the training paragraph after the SSA
+ * output; part (2): mid-training and post-training), which needs dq, dk, dv.
+ * With P_ij = exp(scale q_i.k_j - lse_i) over the attended pairs and
+ * D_i = sum_d dout_id o_id:
+ *     dq_i = scale sum_j P_ij (dout_i.v_j - D_i) k_j
+ *     dk_j = scale sum_i P_ij (dout_i.v_j - D_i) q_i
+ *     dv_j = sum_i P_ij dout_i
+ * summed over every query head of a kv head's group for dk and dv.
+ *
+ *   q, k, v    the forward's inputs, layouts as in ssa_prefill.
+ *   o, lse     the forward's output [batch, seq_len, heads_q, d_v] (strides
+ *              o_strides) and its lse [batch, heads_q, seq_len] (fp32,
+ *              contiguous, natural log), as written by ssa_prefill; lse is
+ *              required here.
+ *   dout       upstream gradient, shape of o, strides do_strides.
+ *   dq, dk, dv written, shapes of q, k, v with their own strides; every
+ *              element is overwritten (no accumulation into old contents).
+ *              They must not overlap any input.
+ *   workspace  device scratch of at least ssa_prefill_backward_workspace_size
+ *              bytes; no initial contents are required; calls sharing one
+ *              workspace must not overlap.
+ * Accumulation is fp32; P and the score gradients are rounded to bf16 as
+ * MFMA operands. Results are deterministic (no atomics). batch == 0 or
+ * seq_len == 0 is a no-op. Compiled: bf16 with (d_qk, d_v) = (64,64),
+ * (128,128), (192,128); anything else returns SSA_ERR_UNSUPPORTED.
+ */
+ssa_status ssa_prefill_backward(ssa_dtype dtype, const void *q, const void *k, const void *v,
+                                const void *o, const float *lse, const void *dout, void *dq,
+                                void *dk, void *dv, int32_t batch, int32_t seq_len,
+                                int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                                const int64_t q_strides[3], const int64_t k_strides[3],
+                                const int64_t v_strides[3], const int64_t o_strides[3],
+                                const int64_t do_strides[3], const int64_t dq_strides[3],
+                                const int64_t dk_strides[3], const int64_t dv_strides[3],
+                                void *workspace, size_t workspace_bytes, ssa_pattern pattern,
+                                float scale, hipStream_t stream);
+
+/*
+ * Workspace bytes for ssa_prefill_backward with the same shape arguments;
+ * 0 for arguments it would reject and for an empty problem. It holds two
+ * floats per (batch, query head, row) and, when the pattern has sink blocks,
+ * fp32 partial sums of the sink keys' dk and dv per chunk of query rows.
+ */
+size_t ssa_prefill_backward_workspace_size(ssa_dtype dtype, int32_t batch, int32_t seq_len,
+                                           int32_t heads_q, int32_t heads_kv, int32_t d_qk,
+                                           int32_t d_v, ssa_pattern pattern);
+
+/*
  * ssa_decode - one new query token per sequence against a paged KV cache,
  * attending to the SSA window (digest section 02: the streaming sparse
  * attention kernel in the decode phase).

@@ -105,3 +105,27 @@ def compact_paged(k_cache, v_cache, table_np, lens, page_size, block, sink, loca
         if phys.size:
             vc[:phys.size] = vh
     return kc, vc, new_table
+
+
+def assert_grad_parity(out: torch.Tensor, ref: np.ndarray, what: str = ""):
+    """bf16 gradient parity. The relative Frobenius bar is the forward's
+    (5e-3). The absolute bar is the forward's 2e-2 scaled by the tensor's
+    magnitude when that exceeds 1: a gradient entry is a sum over many rows
+    (a sink key's dv collects P_ij dout_i from every later row, with the early
+    rows weighted near 1, and reaches a few units), and bf16 rounding of the
+    P / dS operands and of the output errs in proportion to that sum."""
+    got = as_f64(out)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    if not ref.size:
+        return 0.0, 0.0
+    err = np.abs(got - ref)
+    max_abs = float(err.max())
+    scale = max(1.0, float(np.abs(ref).max()))
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    where = np.unravel_index(int(err.argmax()), err.shape)
+    msg = (f"{what}: max |err| {max_abs:.3e} at {where} (ref {ref[where]:.4g}), "
+           f"bound {BF16_MAX_ABS * scale:.3e}; rel Frobenius {rel:.3e}")
+    assert max_abs <= BF16_MAX_ABS * scale, msg
+    assert rel <= BF16_REL_FRO, msg
+    return max_abs, rel

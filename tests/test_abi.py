@@ -122,3 +122,48 @@ def test_workspace_sizes():
         -(-slots * 512 * 4 // 256) * 256 + slots * 4
     assert ws(torch.bfloat16, 1, 4, 3, 128, 128, 128, 8) == 0          # invalid heads
     assert ws(torch.bfloat16, 1, 4, 4, 128, 128, 128, 8, local=0) == 0
+
+
+def backward_call(dtype=1, B=1, N=256, Hq=4, Hkv=4, dqk=128, dv=128, pattern=(128, 1, 7),
+                  scale=0.1, ptr=FAKE, lse=FAKE, ws_bytes=1 << 30, st=None):
+    lib = ssa.load_library()
+    s = st or strides(N * Hq * dqk, Hq * dqk, dqk)
+    p = ctypes.c_void_p(ptr) if ptr is not None else None
+    lp = ctypes.c_void_p(lse) if lse is not None else None
+    return lib.ssa_prefill_backward(dtype, p, p, p, p, lp, p, p, p, p, B, N, Hq, Hkv, dqk, dv,
+                                    s, s, s, s, s, s, s, s, p, ws_bytes,
+                                    ssa.Pattern(*pattern), scale, None)
+
+
+def test_backward_validation():
+    assert backward_call(dtype=5) == INVALID
+    assert backward_call(Hq=4, Hkv=3) == INVALID
+    assert backward_call(pattern=(128, 1, 0)) == INVALID
+    assert backward_call(scale=math.nan) == INVALID
+    assert backward_call(ptr=None) == INVALID
+    assert backward_call(lse=None) == INVALID                 # the forward's lse is required
+    assert backward_call(ptr=FAKE + 2) == INVALID
+    assert backward_call(st=strides(1024, 3, 1)) == INVALID
+    assert backward_call(dtype=0) == UNSUPPORTED              # fp32 backward is not compiled
+    assert backward_call(dqk=96, dv=96) == UNSUPPORTED
+    assert backward_call(ws_bytes=64) == WORKSPACE
+    assert backward_call(B=0, ptr=None, lse=None) == OK
+    assert backward_call(N=0, ptr=None, lse=None) == OK
+
+
+def test_backward_workspace_sizes():
+    import torch
+    ws = ssa.backward_workspace_size
+    # 32K tokens, 16 heads, b=128 s=1 l=7: row statistics (2 floats per row and
+    # head) + partial sums of the 128 sink keys over ceil(32768 / 3584) = 10
+    # chunks of 4 * 7 * 128 rows.
+    rowstat = 16 * 32768 * 2 * 4
+    part = 10 * 16 * 128 * (128 + 128) * 4
+    assert ws(torch.bfloat16, 1, 32768, 16, 16, 128, 128) == rowstat + part
+    # no sink: row statistics only, rows padded to 128
+    assert ws(torch.bfloat16, 2, 1000, 4, 2, 64, 64, sink=0, local=3) == 2 * 4 * 1024 * 2 * 4
+    # short sequence: one chunk (rows padded to 128), sink keys clamped to N
+    assert ws(torch.bfloat16, 1, 100, 2, 2, 192, 128) == -(-2 * 128 * 2 * 4 // 256) * 256 + \
+        1 * 2 * 100 * 320 * 4
+    assert ws(torch.float32, 1, 100, 2, 2, 128, 128) == 0    # not compiled
+    assert ws(torch.bfloat16, 1, 100, 3, 2, 128, 128) == 0   # invalid heads
