@@ -7,13 +7,14 @@ counted as algorithmic flops 2*(d_qk + d_v) per attended (query, key) pair.
 The same line carries the other workloads of the metric: prefill at 2K (fp32)
 and 256K tokens, SSA and full-attention decode on the 128K-context latent
 workload and SSA decode on the ragged 4K-1M workload (HBM GB/s of algorithmic
-bytes), each against its roofline, and the CPU oracle timed on the prefill.
+bytes), the prefill backward at 32K and 256K tokens (TFLOP/s), each against
+its roofline, and the CPU oracle timed on the prefill.
 
 Inputs are synthetic (seeded N(0,1)) and resident in HBM before timing.
 Timing uses HIP events recorded on the stream the kernels are launched on
 (torch's current stream, which the binding passes to the library).
 
---profile {prefill,decode,copy} runs one short workload and prints nothing
+--profile {prefill,decode,backward,copy} runs one short workload and prints nothing
 else, for rocprofv3 counter collection (copy: a plain 1 GiB device copy whose
 counter readings calibrate FETCH_SIZE / WRITE_SIZE).
 """
@@ -183,6 +184,60 @@ def bench_prefill(cfg_id: int, steps: int, warmup: int):
     del step
     free_gpu()
     return cfg, res
+
+
+# ---------------------------------------------------------------------------
+# Backward of prefill
+# ---------------------------------------------------------------------------
+def backward_flops(cfg) -> int:
+    """Algorithmic flops of the backward: per attended pair and head, the
+    recomputed scores (2 d_qk), dP = dout.v (2 d_v), dv (2 d_v), dk (2 d_qk)
+    and dq (2 d_qk)."""
+    from block_sparse_streaming_amd import inputs
+    pairs = attended_pairs(cfg.N, **inputs.PATTERN) * cfg.Hq * cfg.B
+    return pairs * 2 * (3 * cfg.d_qk + 2 * cfg.d_v)
+
+
+def backward_setup(cfg_id: int):
+    import torch
+    import block_sparse_streaming_amd as ssa
+    from block_sparse_streaming_amd import inputs
+
+    cfg = inputs.CONFIGS[cfg_id]
+    q, k, v = inputs.prefill_inputs(cfg, "cuda:0")
+    do = inputs.prefill_grad(cfg, "cuda:0")
+    o, lse = ssa.prefill(q, k, v, **inputs.PATTERN, scale=cfg.scale, return_lse=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = ssa.backward_workspace_size(cfg.dtype, cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.d_qk, cfg.d_v,
+                                       **inputs.PATTERN)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        ssa.prefill_backward(q, k, v, o, lse, do, **inputs.PATTERN, scale=cfg.scale, dq=dq, dk=dk,
+                             dv=dv, workspace=ws)
+
+    return cfg, step
+
+
+def bench_backward(cfg_id: int, steps: int, warmup: int):
+    """ssa_prefill_backward (three launches: dq, dk/dv, sink finalize) on a
+    prefill workload, given the forward's o and lse."""
+    import torch
+    cfg, step = backward_setup(cfg_id)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_events(step, steps)
+    flops = backward_flops(cfg)
+    tflops = flops / (ms * 1e-3) / 1e12
+    name = cfg.name.replace("prefill", "backward", 1)
+    res = {"workload": name, "ms": ms, "steps": steps, "algorithmic_flops": flops, "TFLOP/s": tflops,
+           "roofline": with_measured({"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                                      "traffic": None})}
+    del step
+    free_gpu()
+    return name, res
 
 
 # ---------------------------------------------------------------------------
@@ -360,6 +415,10 @@ def profile_run(what: str):
             step()
     elif what == "decode":
         bench_decode_latent(64)
+    elif what == "backward":
+        _, step = backward_setup(2)
+        for _ in range(3):
+            step()
     elif what == "copy":
         n = 1 << 28                                   # 1 GiB of fp32 each way
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -374,7 +433,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--profile", choices=["prefill", "decode", "copy"], default=None)
+    ap.add_argument("--profile", choices=["prefill", "decode", "backward", "copy"], default=None)
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the 32K prefill (and the CPU oracle)")
     args = ap.parse_args()
@@ -415,6 +474,10 @@ def main():
         workloads[rag["workload"]] = rag
         note(f"decode {rag['workload']}: ssa {rag['ssa_decode']['us']:.2f} us "
              f"({rag['ssa_decode']['GB/s']:.0f} GB/s)")
+        for cid, steps in ((2, 20), (4, 3)):
+            name, r = bench_backward(cid, steps, 2)
+            workloads[name] = r
+            note(f"backward {name}: {r['ms']:.4f} ms/call, {r['TFLOP/s']:.1f} TFLOP/s")
     cpu = cpu_baseline()
     note(f"cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
     from block_sparse_streaming_amd import inputs

@@ -34,6 +34,8 @@
 // buffers (tile t+1 in flight while t is computed). Tiles read both row-wise
 // and transposed share one XOR swizzle that keeps both patterns free of bank
 // conflicts.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
@@ -43,18 +45,18 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRows = 64;  // query rows per dk/dv sub-tile
+// LDS operand reads issued this many MFMAs ahead of their use: the compiler
+// otherwise reads each operand just before its MFMA and waits out the LDS
+// latency, which one wave per SIMD cannot hide.
+constexpr int kLead = 3;
 
-// Register budgets. dq holds q, dO (B operands) and the dq accumulators per
-// lane: two work-groups per CU fit up to d_qk = 128 with everything in VGPRs;
-// at d_qk = 192 one work-group per CU, with the operands parked in AGPRs.
-// dk/dv holds K, V (parked in AGPRs) and both accumulators: two work-groups
-// per CU only for d_qk + d_v < 256.
+// Register budget of dq: q, dO (B operands) and the dq accumulators per lane.
+// Two work-groups per CU fit up to d_qk = 128 with everything in VGPRs; at
+// d_qk = 192 one work-group per CU, with the operands parked in AGPRs.
 template <int DQK>
 constexpr bool kParkDq = DQK > 128;
 template <int DQK>
 constexpr int kDqOccupancy = DQK > 128 ? 1 : 2;
-template <int DQK, int DV>
-constexpr int kDkvOccupancy = DQK + DV < 256 ? 2 : 1;
 
 // XOR swizzle, in 16-byte units, of row `row` of a bf16 tile with C units per
 // row. Two read patterns must hit distinct banks: 16 consecutive rows at one
@@ -241,17 +243,30 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqacc[d][r] = 0.f;
 
-    const uint32_t k_row = (uint32_t)l32 * RBK, kz = (uint32_t)((hi ^ dual_swz<CK>(l32)) << 4);
-    const uint32_t v_row = (uint32_t)l32 * RBV, vz = (uint32_t)((hi ^ dual_swz<CV>(l32)) << 4);
+    // LDS byte offsets that depend only on the lane, computed once; each read
+    // then takes its block offset as an immediate: operand reads of K / V rows
+    // for the column groups ks & 7 (ks >> 3 adds 256 bytes), and transpose
+    // reads of each 32-column block of K.
+    constexpr int NKO = NQ < 8 ? NQ : 8, NVO = NV < 8 ? NV : 8;
+    uint32_t k_op[NKO], v_op[NVO], k_tr[NDQ];
+    {
+        const uint32_t kz = (uint32_t)((hi ^ dual_swz<CK>(l32)) << 4);
+        const uint32_t vz = (uint32_t)((hi ^ dual_swz<CV>(l32)) << 4);
+#pragma unroll
+        for (int m = 0; m < NKO; ++m) k_op[m] = (uint32_t)l32 * RBK + operand_off<CK>(m, kz);
+#pragma unroll
+        for (int m = 0; m < NVO; ++m) v_op[m] = (uint32_t)l32 * RBV + operand_off<CV>(m, vz);
+#pragma unroll
+        for (int dd = 0; dd < NDQ; ++dd) k_tr[dd] = tr_lane_off<CK>(lane, dd);
+    }
     const int jl = 4 * hi;  // key offset of this lane's accumulator rows
 
     const int r_first = tr.q0 + wave * 32;
     const int r_last = r_first + 31 < a.N - 1 ? r_first + 31 : a.N - 1;
     const int lo_first_w = local_start(a, r_first), lo_last_w = local_start(a, r_last);
 
-    auto compute = [&](int t) {
-        const uint16_t *kb = k_lds[t & 1];
-        const uint16_t *vb = v_lds[t & 1];
+    auto compute = [&](auto buf, int t) {
+        constexpr int BUF = decltype(buf)::value;
         const SubTile st = sub_tile(tr, t);
         const bool local = t >= tr.n_sink;
         const int kend = st.j0 + kBN < st.re ? st.j0 + kBN : st.re;
@@ -259,48 +274,49 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
         const bool full = st.j0 + kBN <= st.re && (!local || st.j0 >= lo_last_w);
         const bool no_mask = full && st.j0 + kBN - 1 <= r_first;
         const bool causal_only = full && !no_mask;
-        // Re-derive the lane offsets here (the empty asm hides their origin)
-        // so that address arithmetic is not hoisted out of the pipelined loop
-        // into registers that would stay live across it.
-        uint32_t k_off = k_row, kzz = kz, v_off = v_row, vzz = vz, lane_r = (uint32_t)lane;
-        asm volatile("" : "+v"(k_off), "+v"(kzz), "+v"(v_off), "+v"(vzz), "+v"(lane_r));
-        const char *kc = (const char *)kb;
-        const char *vc = (const char *)vb;
+        const char *kc = (const char *)k_lds[BUF];
+        const char *vc = (const char *)v_lds[BUF];
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk) {
             if (st.j0 + 32 * kbk > r_last) break;  // the wave's rows precede these keys
             f32x16 sacc, pacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
-            const char *krow = kc + k_off + kbk * 32 * RBK;
-            const char *vrow = vc + v_off + kbk * 32 * RBV;
 #pragma unroll
             for (int ks = 0; ks < NQ; ++ks) {
-                const bf16x8 kf = *(const bf16x8 *)(krow + operand_off<CK>(ks, kzz));
+                const bf16x8 kf = *(const bf16x8 *)(kc + k_op[ks & 7] + (ks >> 3) * 256 + kbk * 32 * RBK);
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
             }
 #pragma unroll
             for (int ks = 0; ks < NV; ++ks) {
-                const bf16x8 vf = *(const bf16x8 *)(vrow + operand_off<CV>(ks, vzz));
+                const bf16x8 vf = *(const bf16x8 *)(vc + v_op[ks & 7] + (ks >> 3) * 256 + kbk * 32 * RBV);
                 pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[ks], pacc, 0, 0, 0);
             }
-            // dS^T: accumulator element r is key kbk*32 + 8(r/4) + 4hi + r%4.
+            // dS^T: accumulator element r is key jb + 8(r/4) + r%4, jb the
+            // block's first key plus 4 hi. MODE 0: no mask; 1: causal only
+            // (key offset <= d0); 2: the full rule.
             float ds[16];
-            const int d0 = i - (st.j0 + jl + 32 * kbk);
             const int jb = st.j0 + jl + 32 * kbk;
+            auto finish = [&](auto mode) {
+                constexpr int MODE = decltype(mode)::value;
+                const int d0 = i - jb;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kk = 8 * (r >> 2) + (r & 3);
-                float p = fast_exp2(__builtin_fmaf(sacc[r], a.scale_log2, -lse2));
-                if (causal_only) {
-                    p = kk <= d0 ? p : 0.f;
-                } else if (!no_mask) {
-                    const int j = jb + kk;
-                    const bool ok = (j < st.re) & (j <= i) & ((j < tr.sb) | (j >= lo_i));
-                    p = ok ? p : 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = 8 * (r >> 2) + (r & 3);
+                    float p = fast_exp2(__builtin_fmaf(sacc[r], a.scale_log2, -lse2));
+                    if constexpr (MODE == 1) {
+                        p = kk <= d0 ? p : 0.f;
+                    } else if constexpr (MODE == 2) {
+                        const int j = jb + kk;
+                        const bool ok = (j < st.re) & (j <= i) & ((j < tr.sb) | (j >= lo_i));
+                        p = ok ? p : 0.f;
+                    }
+                    ds[r] = p * (pacc[r] - dsum);
                 }
-                ds[r] = p * (pacc[r] - dsum);
-            }
+            };
+            if (no_mask) finish(std::integral_constant<int, 0>());
+            else if (causal_only) finish(std::integral_constant<int, 1>());
+            else finish(std::integral_constant<int, 2>());
             // dq^T += K^T dS^T. Instruction c consumes keys 16c + {0..3, 8..11}
             // (+4 on the upper half-wave): accumulator elements 8c..8c+7.
 #pragma unroll
@@ -309,19 +325,19 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
                 const uint32_t blk = (uint32_t)(kbk * 32 + 16 * c) * RBK;
 #pragma unroll
                 for (int dd = 0; dd < NDQ; ++dd)
-                    dqacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CK>(kc, tr_lane_off<CK>((int)lane_r, dd), blk),
-                                                                        sf, dqacc[dd], 0, 0, 0);
+                    dqacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CK>(kc, k_tr[dd], blk), sf,
+                                                                        dqacc[dd], 0, 0, 0);
             }
         }
     };
 
-    // Two-buffer ring: sub-tile t+1 streams in while t is computed. The
-    // transfers are invisible to the compiler, so the explicit wait (all but
-    // the newest sub-tile's transfers done) and the barriers alone order the
-    // buffers.
+    // Two-buffer ring, unrolled by two so that each buffer's LDS address is a
+    // constant of its compute body: sub-tile t+1 streams in while t is
+    // computed. The transfers are invisible to the compiler, so the explicit
+    // wait (all but the newest sub-tile's transfers done) and the barriers
+    // alone order the buffers.
     const int T = tr.n_total;
-    if (T > 0) issue(0);
-    for (int t = 0; t < T; ++t) {
+    auto step = [&](auto buf, int t) {
         if (t + 1 < T) {
             issue(t + 1);
             wait_vmcnt<NDMA>();
@@ -329,8 +345,13 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
             wait_vmcnt<0>();
         }
         barrier_no_fence();
-        compute(t);
+        compute(buf, t);
         barrier_lds_drained();
+    };
+    if (T > 0) issue(0);
+    for (int t = 0; t < T; t += 2) {
+        step(std::integral_constant<int, 0>(), t);
+        if (t + 1 < T) step(std::integral_constant<int, 1>(), t + 1);
     }
 
     if (row_ok) {
@@ -352,27 +373,42 @@ __device__ __forceinline__ int key_row_end(const BackwardArgs &a, int j) {
     return (int)(e < a.N ? e : a.N);
 }
 
+// The dk/dv work-group: 128 keys of one kv head, 4 waves of 32 keys. A wave
+// holds its keys' K and V rows and both accumulators, more than half the
+// register file, so each SIMD runs one wave: the LDS operand reads are issued
+// ahead of their MFMAs by hand and the query-row tiles stream in through a
+// two-buffer ring. (Splitting dv and dk over two waves per SIMD, which must
+// then both compute S, measured slower.)
 template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads, (kDkvOccupancy<DQK, DV>)) void ssa_bwd_dkv_bf16(const BackwardArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardArgs a) {
+    constexpr int NW = kThreads / 64;
     constexpr int CQ = DQK / 8, CD = DV / 8;   // 16-byte units per q / dO row
-    constexpr int NIQ = CQ / 4, NID = CD / 4;  // transfers per wave per sub-tile
-    constexpr int NDMA = NIQ + NID + 1;        // + the row statistics
+    static_assert(CQ % NW == 0 && CD % NW == 0, "tile rows must split into whole waves");
+    // A 64-row tile is CQ (CD) transfers of 64 lanes x 16 bytes, shared out
+    // over the waves; the 512 bytes of row statistics likewise.
+    constexpr int NIQ = CQ / NW, NID = CD / NW;
+    constexpr int NDMA = NIQ + NID + 1;
     constexpr int NQ = DQK / 16, NV = DV / 16, NDK = DQK / 32, NDV = DV / 32;
     constexpr uint32_t RBQ = DQK * 2, RBD = DV * 2;
-    static_assert(CQ % 4 == 0 && CD % 4 == 0, "tile rows must split into whole waves");
+    constexpr int NB = 2;
     constexpr uint32_t QBUF = kRows * DQK * 2, DBUF = kRows * DV * 2;  // bytes per buffer
-    __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][kRows * DQK];
-    __shared__ __attribute__((aligned(1024))) uint16_t d_lds[2][kRows * DV];
-    __shared__ __attribute__((aligned(16))) float s_lds[2][128];  // lse * log2 e [64], D [64]
+    __shared__ __attribute__((aligned(1024))) uint16_t q_lds[NB][kRows * DQK];
+    __shared__ __attribute__((aligned(1024))) uint16_t d_lds[NB][kRows * DV];
+    __shared__ __attribute__((aligned(16))) float s_lds[NB][128];  // lse * log2 e [64], D [64]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
 
     // Work-groups [0, n_part): (chunk, sink key tile, kv head, batch); the
-    // rest: (key tile past the sink tiles, kv head, batch).
-    const int wg = xcd_remap(blockIdx.x, a.dkv_wgs);
+    // rest: (key tile past the sink tiles, kv head, batch). A sink chunk does
+    // several times the work of an ordinary key tile, so the chunks keep the
+    // dispatch order, which deals them out over the XCDs in turn; only the
+    // ordinary tiles are renumbered so that each XCD runs a contiguous run of
+    // key tiles (neighbours read the same query rows from its L2).
     const int n_part = a.sink_tiles * a.n_chunks * a.Hkv * a.B;
+    const int bid = blockIdx.x;
+    const int wg = bid < n_part ? bid : n_part + xcd_remap(bid - n_part, a.dkv_wgs - n_part);
     const bool part = wg < n_part;
     int kt, g, bb, ch = 0, r0, r1;
     if (part) {
@@ -424,13 +460,11 @@ __global__ __launch_bounds__(kThreads, (kDkvOccupancy<DQK, DV>)) void ssa_bwd_dk
             if (key_ok) w = *(const u32x4 *)(vrow + ks * 16);
             vf[ks] = __builtin_bit_cast(bf16x8, w);
         }
-        if constexpr (kDkvOccupancy<DQK, DV> == 1) {
-            // Read-only MFMA operands live in AGPRs for the whole work-group.
+        // Read-only MFMA operands live in AGPRs for the whole work-group.
 #pragma unroll
-            for (int ks = 0; ks < NQ; ++ks) asm volatile("" : "+a"(kf[ks]));
+        for (int ks = 0; ks < NQ; ++ks) asm volatile("" : "+a"(kf[ks]));
 #pragma unroll
-            for (int ks = 0; ks < NV; ++ks) asm volatile("" : "+a"(vf[ks]));
-        }
+        for (int ks = 0; ks < NV; ++ks) asm volatile("" : "+a"(vf[ks]));
     }
     // Wave-uniform bounds: first and last valid key of the wave, and the
     // least and greatest row end over its keys. Sink keys are attended up to
@@ -455,9 +489,10 @@ __global__ __launch_bounds__(kThreads, (kDkvOccupancy<DQK, DV>)) void ssa_bwd_dk
     const uint32_t q_lds0 = lds_addr(&q_lds[0][0]), d_lds0 = lds_addr(&d_lds[0][0]);
     const uint32_t s_lds0 = lds_addr(&s_lds[0][0]);
     auto issue = [&](int t) {
-        const uint32_t qb = __builtin_amdgcn_readfirstlane(q_lds0 + (t & 1) * QBUF);
-        const uint32_t db = __builtin_amdgcn_readfirstlane(d_lds0 + (t & 1) * DBUF);
-        const uint32_t sb = s_lds0 + (t & 1) * 512u;
+        const int slot = t % NB;
+        const uint32_t qb = __builtin_amdgcn_readfirstlane(q_lds0 + slot * QBUF);
+        const uint32_t db = __builtin_amdgcn_readfirstlane(d_lds0 + slot * DBUF);
+        const uint32_t sbuf = s_lds0 + slot * 512u;
         const int hh = g * a.group + t / nsub;
         const int i0 = r0 + kRows * (t % nsub);
         const int rows_valid = r1 - i0 < kRows ? r1 - i0 : kRows;
@@ -473,35 +508,57 @@ __global__ __launch_bounds__(kThreads, (kDkvOccupancy<DQK, DV>)) void ssa_bwd_dk
             const int p = (wave * NID + n) * 64 + lane;
             dma16_untracked(dt + dma_off<CD>(p, ds1i, rows_valid), db + (wave * NID + n) * 1024);
         }
-        // Row statistics of rows i0..i0+63 (512 contiguous bytes): 128 per wave.
-        const float *src = a.rowstat + (((int64_t)bb * a.Hq + hh) * rs_groups + (i0 >> 6)) * 128 + wave * 32 + 4 * lane;
-        const uint32_t s_dst = __builtin_amdgcn_readfirstlane(sb + wave * 128);
-        if (lane < 8) dma16_untracked(src, s_dst);
+        // Row statistics of rows i0..i0+63: 512 contiguous bytes, 512 / NW per wave.
+        constexpr int SF = 128 / NW;  // floats per wave
+        // (the lane offset is re-derived per transfer rather than kept as a
+        // 64-bit per-lane pointer across the loop)
+        uint32_t s_lane = (uint32_t)(wave * SF + 4 * lane);
+        asm volatile("" : "+v"(s_lane));
+        const float *src = a.rowstat + (((int64_t)bb * a.Hq + hh) * rs_groups + (i0 >> 6)) * 128 + s_lane;
+        const uint32_t s_dst = __builtin_amdgcn_readfirstlane(sbuf + wave * SF * 4);
+        if (lane < SF / 4) dma16_untracked(src, s_dst);
     };
 
-    f32x16 dkacc[NDK], dvacc[NDV];
-#pragma unroll
-    for (int d = 0; d < NDK; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dkacc[d][r] = 0.f;
+    f32x16 dvacc[NDV], dkacc[NDK];
 #pragma unroll
     for (int d = 0; d < NDV; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dvacc[d][r] = 0.f;
+#pragma unroll
+    for (int d = 0; d < NDK; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dkacc[d][r] = 0.f;
 
-    const uint32_t q_row = (uint32_t)l32 * RBQ, qz = (uint32_t)((hi ^ dual_swz<CQ>(l32)) << 4);
-    const uint32_t d_row = (uint32_t)l32 * RBD, dz = (uint32_t)((hi ^ dual_swz<CD>(l32)) << 4);
+    // LDS byte offsets that depend only on the lane, computed once (one wave
+    // per SIMD leaves registers to spare): operand reads of q / dO rows for
+    // the column groups ks & 7 (ks >> 3 adds 256 bytes), and transpose reads
+    // of each 32-column block; each read then takes its block offset as an
+    // immediate.
+    constexpr int NQO = NQ < 8 ? NQ : 8, NVO = NV < 8 ? NV : 8;
+    uint32_t q_op[NQO], d_op[NVO], q_tr[NDK], d_tr[NDV];
+    {
+        const uint32_t qz = (uint32_t)((hi ^ dual_swz<CQ>(l32)) << 4);
+        const uint32_t dz = (uint32_t)((hi ^ dual_swz<CD>(l32)) << 4);
+#pragma unroll
+        for (int m = 0; m < NQO; ++m) q_op[m] = (uint32_t)l32 * RBQ + operand_off<CQ>(m, qz);
+#pragma unroll
+        for (int m = 0; m < NVO; ++m) d_op[m] = (uint32_t)l32 * RBD + operand_off<CD>(m, dz);
+#pragma unroll
+        for (int dd = 0; dd < NDK; ++dd) q_tr[dd] = tr_lane_off<CQ>(lane, dd);
+#pragma unroll
+        for (int dd = 0; dd < NDV; ++dd) d_tr[dd] = tr_lane_off<CD>(lane, dd);
+    }
+    // Attended-pair test of row i against this lane's key: j <= i < up_j,
+    // i.e. (unsigned)(i - j) < span.
+    const uint32_t span = up_j > j ? (uint32_t)(up_j - j) : 0u;
 
-    auto compute = [&](int t) {
+    auto compute = [&](auto buf, int t) {
+        constexpr int BUF = decltype(buf)::value;
         if (!wave_live) return;
-        const uint16_t *qb = q_lds[t & 1];
-        const uint16_t *db = d_lds[t & 1];
-        const float *sb = s_lds[t & 1];
+        const char *qc = (const char *)q_lds[BUF];
+        const char *dc = (const char *)d_lds[BUF];
+        const float *sbf = s_lds[BUF];
         const int i0 = r0 + kRows * (t % nsub);
-        uint32_t q_off = q_row, qzz = qz, d_off = d_row, dzz = dz, lane_r = (uint32_t)lane;
-        asm volatile("" : "+v"(q_off), "+v"(qzz), "+v"(d_off), "+v"(dzz), "+v"(lane_r));
-        const char *qc = (const char *)qb;
-        const char *dc = (const char *)db;
 #pragma unroll
         for (int qblk = 0; qblk < 2; ++qblk) {
             const int ib = i0 + 32 * qblk;  // first row of the block
@@ -510,60 +567,94 @@ __global__ __launch_bounds__(kThreads, (kDkvOccupancy<DQK, DV>)) void ssa_bwd_dk
             f32x16 sacc, pacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
-            const char *qrow = qc + q_off + qblk * 32 * RBQ;
-            const char *drow = dc + d_off + qblk * 32 * RBD;
+            // S = Q K^T and dP = dO V^T, the two chains interleaved (operand n
+            // alternates q rows and dO rows while both remain); operands are
+            // read kLead MFMAs ahead of their use.
+            {
+                constexpr int NPAIR = NQ < NV ? NQ : NV, NS = NQ + NV;
+                auto kind = [](int n) { return n < 2 * NPAIR ? (n & 1) : (NV > NQ ? 1 : 0); };  // 0: q row
+                auto kidx = [](int n) { return n < 2 * NPAIR ? (n >> 1) : n - NPAIR; };
+                bf16x8 opa[NS];
+                auto load = [&](int n) {
+                    const int ks = kidx(n);
+                    opa[n] = kind(n) == 0
+                                 ? *(const bf16x8 *)(qc + q_op[ks & 7] + (ks >> 3) * 256 + qblk * 32 * RBQ)
+                                 : *(const bf16x8 *)(dc + d_op[ks & 7] + (ks >> 3) * 256 + qblk * 32 * RBD);
+                };
 #pragma unroll
-            for (int ks = 0; ks < NQ; ++ks) {
-                const bf16x8 qa = *(const bf16x8 *)(qrow + operand_off<CQ>(ks, qzz));
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sacc, 0, 0, 0);
-            }
+                for (int n = 0; n < kLead; ++n) load(n);
 #pragma unroll
-            for (int ks = 0; ks < NV; ++ks) {
-                const bf16x8 da = *(const bf16x8 *)(drow + operand_off<CD>(ks, dzz));
-                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], pacc, 0, 0, 0);
-            }
-            // Accumulator element r is row ib + 8(r/4) + 4hi + r%4.
-            float pv[16], ds[16];
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int rl = 32 * qblk + 8 * rq + 4 * hi;  // row within the sub-tile
-                const f32x4 l4 = *(const f32x4 *)(sb + rl);
-                const f32x4 d4 = *(const f32x4 *)(sb + 64 + rl);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * rq + e;
-                    float p = fast_exp2(__builtin_fmaf(sacc[r], a.scale_log2, -l4[e]));
-                    if (!no_mask) {
-                        const int row = ib + 8 * rq + 4 * hi + e;
-                        p = ((row >= j) & (row < up_j)) ? p : 0.f;
-                    }
-                    pv[r] = p;
-                    ds[r] = p * (pacc[r] - d4[e]);
+                for (int n = 0; n < NS; ++n) {
+                    if (n + kLead < NS) load(n + kLead);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int ks = kidx(n);
+                    if (kind(n) == 0) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[n], kf[ks], sacc, 0, 0, 0);
+                    else pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[n], vf[ks], pacc, 0, 0, 0);
                 }
             }
+            // P and dS from the scores, packed to bf16 pairs as they are made;
+            // accumulator element r is row ib + 8(r/4) + 4hi + r%4.
+            u32x4 pw[2], sw[2];
+            auto finish = [&](auto masked) {
+                const uint32_t x = (uint32_t)(ib + 4 * hi - j);
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int rl = 32 * qblk + 8 * rq + 4 * hi;  // row within the sub-tile
+                    const f32x4 l4 = *(const f32x4 *)(sbf + rl);
+                    const f32x4 d4 = *(const f32x4 *)(sbf + 64 + rl);
+                    float p[4], d[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * rq + e;
+                        p[e] = fast_exp2(__builtin_fmaf(sacc[r], a.scale_log2, -l4[e]));
+                        if constexpr (decltype(masked)::value) p[e] = x + (uint32_t)(8 * rq + e) < span ? p[e] : 0.f;
+                        d[e] = p[e] * (pacc[r] - d4[e]);
+                    }
+                    // elements 4rq..4rq+3 are packed words 2rq, 2rq+1
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int w = 2 * rq + h;
+                        pw[w >> 2][w & 3] = pack_bf16x2(p[2 * h], p[2 * h + 1]);
+                        sw[w >> 2][w & 3] = pack_bf16x2(d[2 * h], d[2 * h + 1]);
+                    }
+                }
+            };
+            if (no_mask) finish(std::false_type());
+            else finish(std::true_type());
             // dv^T += dO^T P and dk^T += Q^T dS. Instruction c consumes rows
-            // 16c + {0..3, 8..11} (+4 on the upper half-wave): accumulator
-            // elements 8c..8c+7.
+            // 16c + {0..3, 8..11} (+4 on the upper half-wave): packed words
+            // 4c..4c+3. Operands are read kLead MFMAs ahead of their use.
+            {
+                constexpr int NM = NDV + NDK, NO = 2 * NM;  // operands per c, in all
+                bf16x8 opt[NO];
+                auto load = [&](int n) {
+                    const int c = n / NM, m = n % NM;
+                    const uint32_t row0 = (uint32_t)(qblk * 32 + 16 * c);
+                    opt[n] = m < NDV ? tr_operand<CD>(dc, d_tr[m], row0 * RBD)
+                                     : tr_operand<CQ>(qc, q_tr[m - NDV], row0 * RBQ);
+                };
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const bf16x8 pf = pack8(pv + 8 * c);
-                const bf16x8 sf = pack8(ds + 8 * c);
-                const uint32_t blkq = (uint32_t)(qblk * 32 + 16 * c) * RBQ;
-                const uint32_t blkd = (uint32_t)(qblk * 32 + 16 * c) * RBD;
+                for (int n = 0; n < kLead; ++n) load(n);
 #pragma unroll
-                for (int dd = 0; dd < NDV; ++dd)
-                    dvacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CD>(dc, tr_lane_off<CD>((int)lane_r, dd), blkd),
-                                                                        pf, dvacc[dd], 0, 0, 0);
-#pragma unroll
-                for (int dd = 0; dd < NDK; ++dd)
-                    dkacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CQ>(qc, tr_lane_off<CQ>((int)lane_r, dd), blkq),
-                                                                        sf, dkacc[dd], 0, 0, 0);
+                for (int n = 0; n < NO; ++n) {
+                    if (n + kLead < NO) load(n + kLead);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int c = n / NM, m = n % NM;
+                    if (m < NDV)
+                        dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opt[n], __builtin_bit_cast(bf16x8, pw[c]),
+                                                                           dvacc[m], 0, 0, 0);
+                    else
+                        dkacc[m - NDV] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            opt[n], __builtin_bit_cast(bf16x8, sw[c]), dkacc[m - NDV], 0, 0, 0);
+                }
             }
         }
     };
 
-    if (T > 0) issue(0);
-    for (int t = 0; t < T; ++t) {
+    // Two-buffer ring, unrolled by two so that each buffer's LDS address is
+    // a constant of its compute body: sub-tile t+1 streams in while t is
+    // computed; before computing t, wait for all but the newest transfers.
+    auto step = [&](auto buf, int t) {
         if (t + 1 < T) {
             issue(t + 1);
             wait_vmcnt<NDMA>();
@@ -571,20 +662,29 @@ __global__ __launch_bounds__(kThreads, (kDkvOccupancy<DQK, DV>)) void ssa_bwd_dk
             wait_vmcnt<0>();
         }
         barrier_no_fence();
-        compute(t);
+        compute(buf, t);
         barrier_lds_drained();
+    };
+    if (T > 0) issue(0);
+    for (int t = 0; t < T; t += 2) {
+        step(std::integral_constant<int, 0>(), t);
+        if (t + 1 < T) step(std::integral_constant<int, 1>(), t + 1);
     }
 
     if (!key_ok) return;
+    // The key index passes through an empty asm so that the output addresses
+    // are computed here, not hoisted above the loop into live registers.
+    int je = j;
+    asm volatile("" : "+v"(je));
     if (!part) {
-        uint16_t *dkrow = (uint16_t *)a.dk + bb * a.dks[0] + (int64_t)j * a.dks[1] + g * a.dks[2];
-        uint16_t *dvrow = (uint16_t *)a.dv + bb * a.dvs[0] + (int64_t)j * a.dvs[1] + g * a.dvs[2];
+        uint16_t *dkrow = (uint16_t *)a.dk + bb * a.dks[0] + (int64_t)je * a.dks[1] + g * a.dks[2];
+        uint16_t *dvrow = (uint16_t *)a.dv + bb * a.dvs[0] + (int64_t)je * a.dvs[1] + g * a.dvs[2];
 #pragma unroll
         for (int dd = 0; dd < NDK; ++dd) store_row_block(dkrow, dkacc[dd], dd, hi, a.scale);
 #pragma unroll
         for (int dd = 0; dd < NDV; ++dd) store_row_block(dvrow, dvacc[dd], dd, hi, 1.f);
     } else {
-        float *dst = a.sink_part + ((((int64_t)ch * a.B + bb) * a.Hkv + g) * a.sink_rows + j) * (DQK + DV);
+        float *dst = a.sink_part + ((((int64_t)ch * a.B + bb) * a.Hkv + g) * a.sink_rows + je) * (DQK + DV);
 #pragma unroll
         for (int dd = 0; dd < NDK; ++dd)
 #pragma unroll
