@@ -44,7 +44,6 @@ namespace ssa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 64;  // query rows per dk/dv sub-tile
 // LDS operand reads issued this many MFMAs ahead of their use: the compiler
 // otherwise reads each operand just before its MFMA and waits out the LDS
 // latency, which one wave per SIMD cannot hide.
@@ -282,15 +281,30 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
             f32x16 sacc, pacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+            // S^T = K Q^T and dP^T = V dO^T, the two chains interleaved
+            // (operand n alternates K rows and V rows while both remain);
+            // operands are read kLead MFMAs ahead of their use.
+            {
+                constexpr int NPAIR = NQ < NV ? NQ : NV, NS = NQ + NV;
+                auto kind = [](int n) { return n < 2 * NPAIR ? (n & 1) : (NV > NQ ? 1 : 0); };  // 0: K row
+                auto kidx = [](int n) { return n < 2 * NPAIR ? (n >> 1) : n - NPAIR; };
+                bf16x8 opa[NS];
+                auto load = [&](int n) {
+                    const int ks = kidx(n);
+                    opa[n] = kind(n) == 0
+                                 ? *(const bf16x8 *)(kc + k_op[ks & 7] + (ks >> 3) * 256 + kbk * 32 * RBK)
+                                 : *(const bf16x8 *)(vc + v_op[ks & 7] + (ks >> 3) * 256 + kbk * 32 * RBV);
+                };
 #pragma unroll
-            for (int ks = 0; ks < NQ; ++ks) {
-                const bf16x8 kf = *(const bf16x8 *)(kc + k_op[ks & 7] + (ks >> 3) * 256 + kbk * 32 * RBK);
-                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
-            }
+                for (int n = 0; n < kLead; ++n) load(n);
 #pragma unroll
-            for (int ks = 0; ks < NV; ++ks) {
-                const bf16x8 vf = *(const bf16x8 *)(vc + v_op[ks & 7] + (ks >> 3) * 256 + kbk * 32 * RBV);
-                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[ks], pacc, 0, 0, 0);
+                for (int n = 0; n < NS; ++n) {
+                    if (n + kLead < NS) load(n + kLead);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int ks = kidx(n);
+                    if (kind(n) == 0) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[n], qf[ks], sacc, 0, 0, 0);
+                    else pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa[n], df[ks], pacc, 0, 0, 0);
+                }
             }
             // dS^T: accumulator element r is key jb + 8(r/4) + r%4, jb the
             // block's first key plus 4 hi. MODE 0: no mask; 1: causal only
@@ -319,14 +333,22 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
             else finish(std::integral_constant<int, 2>());
             // dq^T += K^T dS^T. Instruction c consumes keys 16c + {0..3, 8..11}
             // (+4 on the upper half-wave): accumulator elements 8c..8c+7.
+            {
+                const bf16x8 sf[2] = {pack8(ds), pack8(ds + 8)};
+                constexpr int NO = 2 * NDQ;
+                bf16x8 opt[NO];
+                auto load = [&](int n) {
+                    const int c = n / NDQ, dd = n % NDQ;
+                    opt[n] = tr_operand<CK>(kc, k_tr[dd], (uint32_t)(kbk * 32 + 16 * c) * RBK);
+                };
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const bf16x8 sf = pack8(ds + 8 * c);
-                const uint32_t blk = (uint32_t)(kbk * 32 + 16 * c) * RBK;
+                for (int n = 0; n < kLead; ++n) load(n);
 #pragma unroll
-                for (int dd = 0; dd < NDQ; ++dd)
-                    dqacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<CK>(kc, k_tr[dd], blk), sf,
-                                                                        dqacc[dd], 0, 0, 0);
+                for (int n = 0; n < NO; ++n) {
+                    if (n + kLead < NO) load(n + kLead);
+                    __builtin_amdgcn_sched_barrier(0);
+                    dqacc[n % NDQ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opt[n], sf[n / NDQ], dqacc[n % NDQ], 0, 0, 0);
+                }
             }
         }
     };
@@ -384,17 +406,24 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
     constexpr int NW = kThreads / 64;
     constexpr int CQ = DQK / 8, CD = DV / 8;   // 16-byte units per q / dO row
     static_assert(CQ % NW == 0 && CD % NW == 0, "tile rows must split into whole waves");
-    // A 64-row tile is CQ (CD) transfers of 64 lanes x 16 bytes, shared out
-    // over the waves; the 512 bytes of row statistics likewise.
-    constexpr int NIQ = CQ / NW, NID = CD / NW;
+    // Query rows per ring step: 128 where two buffers of them fit in LDS,
+    // which halves the per-step cost of the transfers' issue, the wait and
+    // the barriers; 64 otherwise.
+    constexpr int KR = DQK + DV <= 256 ? 128 : 64;
+    constexpr int NG = KR / 64;  // 64-row groups of row statistics per step
+    // A KR-row tile is (KR / 64) * CQ (CQ: 16-byte units per row) transfers of
+    // 64 lanes x 16 bytes, shared out over the waves; the 512 bytes of row
+    // statistics per 64 rows likewise.
+    constexpr int NIQ = NG * CQ / NW, NID = NG * CD / NW;
     constexpr int NDMA = NIQ + NID + 1;
     constexpr int NQ = DQK / 16, NV = DV / 16, NDK = DQK / 32, NDV = DV / 32;
     constexpr uint32_t RBQ = DQK * 2, RBD = DV * 2;
     constexpr int NB = 2;
-    constexpr uint32_t QBUF = kRows * DQK * 2, DBUF = kRows * DV * 2;  // bytes per buffer
-    __shared__ __attribute__((aligned(1024))) uint16_t q_lds[NB][kRows * DQK];
-    __shared__ __attribute__((aligned(1024))) uint16_t d_lds[NB][kRows * DV];
-    __shared__ __attribute__((aligned(16))) float s_lds[NB][128];  // lse * log2 e [64], D [64]
+    constexpr uint32_t QBUF = KR * DQK * 2, DBUF = KR * DV * 2;  // bytes per buffer
+    __shared__ __attribute__((aligned(1024))) uint16_t q_lds[NB][KR * DQK];
+    __shared__ __attribute__((aligned(1024))) uint16_t d_lds[NB][KR * DV];
+    // per 64 rows: lse * log2 e [64], D [64]
+    __shared__ __attribute__((aligned(16))) float s_lds[NB][NG * 128];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -434,7 +463,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
         r0 = kt * kBM;
         r1 = key_row_end(a, k1 - 1);
     }
-    const int nsub = r1 > r0 ? (r1 - r0 + kRows - 1) / kRows : 0;
+    const int nsub = r1 > r0 ? (r1 - r0 + KR - 1) / KR : 0;
     const int T = a.group * nsub;
 
     // This lane's key: its K and V rows as B operands, and the rows that
@@ -492,10 +521,10 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
         const int slot = t % NB;
         const uint32_t qb = __builtin_amdgcn_readfirstlane(q_lds0 + slot * QBUF);
         const uint32_t db = __builtin_amdgcn_readfirstlane(d_lds0 + slot * DBUF);
-        const uint32_t sbuf = s_lds0 + slot * 512u;
+        const uint32_t sbuf = s_lds0 + slot * (NG * 512u);
         const int hh = g * a.group + t / nsub;
-        const int i0 = r0 + kRows * (t % nsub);
-        const int rows_valid = r1 - i0 < kRows ? r1 - i0 : kRows;
+        const int i0 = r0 + KR * (t % nsub);
+        const int rows_valid = r1 - i0 < KR ? r1 - i0 : KR;
         const char *qt = (const char *)((const uint16_t *)a.q + bb * a.qs[0] + (int64_t)i0 * qs1 + hh * a.qs[2]);
         const char *dt = (const char *)((const uint16_t *)a.dout + bb * a.dos[0] + (int64_t)i0 * ds1 + hh * a.dos[2]);
 #pragma unroll
@@ -508,8 +537,9 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
             const int p = (wave * NID + n) * 64 + lane;
             dma16_untracked(dt + dma_off<CD>(p, ds1i, rows_valid), db + (wave * NID + n) * 1024);
         }
-        // Row statistics of rows i0..i0+63: 512 contiguous bytes, 512 / NW per wave.
-        constexpr int SF = 128 / NW;  // floats per wave
+        // Row statistics of rows i0..i0+KR-1: NG * 512 contiguous bytes
+        // (i0 is a multiple of 128, KR rows stay below n_pad), shared out.
+        constexpr int SF = NG * 128 / NW;  // floats per wave
         // (the lane offset is re-derived per transfer rather than kept as a
         // 64-bit per-lane pointer across the loop)
         uint32_t s_lane = (uint32_t)(wave * SF + 4 * lane);
@@ -558,9 +588,9 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
         const char *qc = (const char *)q_lds[BUF];
         const char *dc = (const char *)d_lds[BUF];
         const float *sbf = s_lds[BUF];
-        const int i0 = r0 + kRows * (t % nsub);
+        const int i0 = r0 + KR * (t % nsub);
 #pragma unroll
-        for (int qblk = 0; qblk < 2; ++qblk) {
+        for (int qblk = 0; qblk < KR / 32; ++qblk) {
             const int ib = i0 + 32 * qblk;  // first row of the block
             if (ib + 31 < jw_first || ib >= up_max) continue;  // no pair of the wave is attended
             const bool no_mask = ib >= jw_last && ib + 31 < up_min;
@@ -599,9 +629,11 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
                 const uint32_t x = (uint32_t)(ib + 4 * hi - j);
 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq) {
-                    const int rl = 32 * qblk + 8 * rq + 4 * hi;  // row within the sub-tile
-                    const f32x4 l4 = *(const f32x4 *)(sbf + rl);
-                    const f32x4 d4 = *(const f32x4 *)(sbf + 64 + rl);
+                    // row rl of the sub-tile: group rl / 64, lse then D
+                    const int rl = 32 * qblk + 8 * rq + 4 * hi;
+                    const float *st = sbf + (rl >> 6) * 128 + (rl & 63);
+                    const f32x4 l4 = *(const f32x4 *)st;
+                    const f32x4 d4 = *(const f32x4 *)(st + 64);
                     float p[4], d[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
