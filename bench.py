@@ -198,6 +198,27 @@ def backward_flops(cfg) -> int:
     return pairs * 2 * (3 * cfg.d_qk + 2 * cfg.d_v)
 
 
+def backward_kernel_keys(cfg) -> list[str]:
+    """Trace keys (kernel, grid in work-items) of the three backward launches
+    for the deployed pattern, as the library plans them."""
+    from block_sparse_streaming_amd import inputs
+    b, s, l = (inputs.PATTERN[k] for k in ("block", "sink", "local"))
+    n_pad = -(-cfg.N // 128) * 128
+    tiles = n_pad // 128
+    sink_keys = min(s * b, cfg.N)
+    sink_tiles = -(-sink_keys // 128)
+    sink_rows = min(sink_tiles * 128, cfg.N)
+    span = -(-min(l * b, n_pad) // 128) * 128
+    chunk = min(4 * max(span, 128), n_pad)
+    n_chunks = -(-cfg.N // chunk) if sink_tiles else 0
+    dq = tiles * cfg.Hq * cfg.B
+    dkv = (sink_tiles * n_chunks + tiles - sink_tiles) * cfg.Hkv * cfg.B
+    fin = -(-(cfg.B * cfg.Hkv * sink_rows * (cfg.d_qk + cfg.d_v) // 4) // 256)
+    d = f"<{cfg.d_qk}, {cfg.d_v}>"
+    return [f"ssa_bwd_dq_bf16{d} grid={dq * 256}", f"ssa_bwd_dkv_bf16{d} grid={dkv * 256}",
+            f"ssa_bwd_sink_finalize{d} grid={fin * 256}"]
+
+
 def backward_setup(cfg_id: int):
     import torch
     import block_sparse_streaming_amd as ssa
@@ -234,7 +255,7 @@ def bench_backward(cfg_id: int, steps: int, warmup: int):
     res = {"workload": name, "ms": ms, "steps": steps, "algorithmic_flops": flops, "TFLOP/s": tflops,
            "roofline": with_measured({"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                                       "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
-                                      "traffic": None})}
+                                      "traffic": recorded_traffic(backward_kernel_keys(cfg))})}
     del step
     free_gpu()
     return name, res
