@@ -7,14 +7,16 @@ counted as algorithmic flops 2*(d_qk + d_v) per attended (query, key) pair.
 The same line carries the other workloads of the metric: prefill at 2K (fp32)
 and 256K tokens, SSA and full-attention decode on the 128K-context latent
 workload and SSA decode on the ragged 4K-1M workload (HBM GB/s of algorithmic
-bytes), the prefill backward at 32K and 256K tokens (TFLOP/s), each against
-its roofline, and the CPU oracle timed on the prefill.
+bytes), the prefill backward at 32K and 256K tokens (TFLOP/s), the dual
+forward (SSA, full causal attention and their alpha-mix in one pass) at 32K
+(TFLOP/s of full causal attention), each against its roofline, and the CPU
+oracle timed on the prefill.
 
 Inputs are synthetic (seeded N(0,1)) and resident in HBM before timing.
 Timing uses HIP events recorded on the stream the kernels are launched on
 (torch's current stream, which the binding passes to the library).
 
---profile {prefill,decode,backward,copy} runs one short workload and prints nothing
+--profile {prefill,decode,backward,dual,copy} runs one short workload and prints nothing
 else, for rocprofv3 counter collection (copy: a plain 1 GiB device copy whose
 counter readings calibrate FETCH_SIZE / WRITE_SIZE).
 """
@@ -173,7 +175,7 @@ def bench_prefill(cfg_id: int, steps: int, warmup: int):
     tflops = flops / (ms * 1e-3) / 1e12
     bf16 = cfg.dtype == torch.bfloat16
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
-    kernel = (f"ssa_prefill_bf16<{cfg.d_qk}, {cfg.d_v}>" if bf16 else
+    kernel = (f"ssa_prefill_bf16<{cfg.d_qk}, {cfg.d_v}, false>" if bf16 else
               f"ssa_prefill_f32<{cfg.d_qk}, {cfg.d_v}>")
     grid = -(-cfg.N // 128) * cfg.Hq * cfg.B * 256
     res = {"workload": cfg.name, "ms": ms, "steps": steps, "algorithmic_flops": flops,
@@ -184,6 +186,53 @@ def bench_prefill(cfg_id: int, steps: int, warmup: int):
     del step
     free_gpu()
     return cfg, res
+
+
+# ---------------------------------------------------------------------------
+# Dual forward (SSA + full causal attention + alpha-mix, one pass)
+# ---------------------------------------------------------------------------
+DUAL_ALPHA = 0.5
+
+
+def dual_setup(cfg_id: int):
+    import torch
+    import block_sparse_streaming_amd as ssa
+    from block_sparse_streaming_amd import inputs
+
+    cfg = inputs.CONFIGS[cfg_id]
+    q, k, v = inputs.prefill_inputs(cfg, "cuda:0")
+    outs = tuple(torch.empty((cfg.B, cfg.N, cfg.Hq, cfg.d_v), dtype=cfg.dtype, device="cuda:0")
+                 for _ in range(3))
+
+    def step():
+        ssa.prefill_dual(q, k, v, **inputs.PATTERN, scale=cfg.scale, alpha=DUAL_ALPHA, out=outs)
+
+    return cfg, step
+
+
+def bench_dual(cfg_id: int, steps: int, warmup: int):
+    """ssa_prefill_dual: the SSA output, the full causal output and their mix
+    in one launch. Its work is that of full causal attention: N(N+1)/2 pairs
+    per head at 2 (d_qk + d_v) flops each."""
+    import torch
+    cfg, step = dual_setup(cfg_id)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_events(step, steps)
+    flops = cfg.N * (cfg.N + 1) // 2 * cfg.Hq * cfg.B * 2 * (cfg.d_qk + cfg.d_v)
+    tflops = flops / (ms * 1e-3) / 1e12
+    grid = -(-cfg.N // 128) * cfg.Hq * cfg.B * 256
+    kernel = f"ssa_prefill_bf16<{cfg.d_qk}, {cfg.d_v}, true>"
+    name = cfg.name.replace("prefill", "prefill_dual", 1)
+    res = {"workload": name, "ms": ms, "steps": steps, "algorithmic_flops": flops, "TFLOP/s": tflops,
+           "alpha": DUAL_ALPHA,
+           "roofline": with_measured({"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                                      "traffic": recorded_traffic([f"{kernel} grid={grid}"])})}
+    del step
+    free_gpu()
+    return name, res
 
 
 # ---------------------------------------------------------------------------
@@ -440,6 +489,10 @@ def profile_run(what: str):
         _, step = backward_setup(2)
         for _ in range(3):
             step()
+    elif what == "dual":
+        _, step = dual_setup(2)
+        for _ in range(3):
+            step()
     elif what == "copy":
         n = 1 << 28                                   # 1 GiB of fp32 each way
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -454,7 +507,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--profile", choices=["prefill", "decode", "backward", "copy"], default=None)
+    ap.add_argument("--profile", choices=["prefill", "decode", "backward", "dual", "copy"], default=None)
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the 32K prefill (and the CPU oracle)")
     args = ap.parse_args()
@@ -499,6 +552,9 @@ def main():
             name, r = bench_backward(cid, steps, 2)
             workloads[name] = r
             note(f"backward {name}: {r['ms']:.4f} ms/call, {r['TFLOP/s']:.1f} TFLOP/s")
+        name, r = bench_dual(2, 10, 2)
+        workloads[name] = r
+        note(f"dual {name}: {r['ms']:.4f} ms/launch, {r['TFLOP/s']:.1f} TFLOP/s")
     cpu = cpu_baseline()
     note(f"cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
     from block_sparse_streaming_amd import inputs

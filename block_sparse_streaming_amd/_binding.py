@@ -20,7 +20,7 @@ SSA_F32 = 0
 SSA_BF16 = 1
 
 # Exported symbols, in the order include/ssa.h declares them.
-EXPORTS = ("ssa_prefill", "ssa_prefill_backward", "ssa_prefill_backward_workspace_size",
+EXPORTS = ("ssa_prefill", "ssa_prefill_dual", "ssa_prefill_backward", "ssa_prefill_backward_workspace_size",
            "ssa_decode", "full_attn_decode", "ssa_decode_workspace_size", "ssa_status_string")
 
 
@@ -55,6 +55,9 @@ def load_library() -> ctypes.CDLL:
     lib.ssa_prefill.restype = ctypes.c_int
     lib.ssa_prefill.argtypes = [ctypes.c_int, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                 i64p, i64p, i64p, i64p, Pattern, f32, p]
+    lib.ssa_prefill_dual.restype = ctypes.c_int
+    lib.ssa_prefill_dual.argtypes = [ctypes.c_int, p, p, p, p, p, p, p, p, f32, i32, i32, i32, i32,
+                                     i32, i32, i64p, i64p, i64p, i64p, Pattern, f32, p]
     lib.ssa_prefill_backward.restype = ctypes.c_int
     lib.ssa_prefill_backward.argtypes = [ctypes.c_int, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                          i32, i32, i64p, i64p, i64p, i64p, i64p, i64p, i64p, i64p,
@@ -143,6 +146,48 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, block: int = 1
                            d_v, _strides3(q), _strides3(k), _strides3(v), _strides3(out),
                            Pattern(block, sink, local), float(scale), _stream(q.device)))
     return (out, lse) if return_lse else out
+
+
+def prefill_dual(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, block: int = 128,
+                 sink: int = 1, local: int = 7, scale: float | None = None,
+                 alpha: float | None = None, return_lse: bool = False, out=None):
+    """ssa_prefill_dual: SSA and full causal attention of the same inputs in
+    one pass. Returns (o_ssa, o_full) and, when ``alpha`` is given, o_mix =
+    alpha * o_full + (1 - alpha) * o_ssa after them; with ``return_lse`` the
+    two lse tensors [B, Hq, N] follow. ``out`` may hold preallocated
+    (o_ssa, o_full, o_mix) tensors of one layout (o_mix may be None)."""
+    lib = load_library()
+    _on_gpu(q, k, v)
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    B, N, Hq, d_qk = q.shape
+    Hkv, d_v = k.shape[2], v.shape[3]
+    if k.shape != (B, N, Hkv, d_qk) or v.shape != (B, N, Hkv, d_v):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if out is None:
+        mk = lambda: torch.empty((B, N, Hq, d_v), dtype=q.dtype, device=q.device)  # noqa: E731
+        o_ssa, o_full = mk(), mk()
+        o_mix = mk() if alpha is not None else None
+    else:
+        o_ssa, o_full, o_mix = out
+        for t in (o_ssa, o_full) + ((o_mix,) if o_mix is not None else ()):
+            _on_gpu(t)
+            if t.shape != (B, N, Hq, d_v) or t.dtype != q.dtype or t.stride() != o_ssa.stride():
+                raise ValueError("outputs must be [B, N, Hq, d_v] of q's dtype with one layout")
+        if (o_mix is None) != (alpha is None):
+            raise ValueError("give alpha exactly when an o_mix buffer is given")
+    lse = [torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if return_lse else None
+           for _ in range(2)]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    _check(lib.ssa_prefill_dual(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o_ssa), _ptr(lse[0]),
+                                _ptr(o_full), _ptr(lse[1]), _ptr(o_mix),
+                                float(alpha if alpha is not None else 0.0), B, N, Hq, Hkv, d_qk,
+                                d_v, _strides3(q), _strides3(k), _strides3(v), _strides3(o_ssa),
+                                Pattern(block, sink, local), float(scale), _stream(q.device)))
+    res = (o_ssa, o_full) + ((o_mix,) if o_mix is not None else ())
+    return res + tuple(lse) if return_lse else res
 
 
 def backward_workspace_size(dtype: torch.dtype, batch: int, seq_len: int, heads_q: int,

@@ -204,16 +204,15 @@ bool backward_shape_ok(ssa_dtype dtype, int32_t batch, int32_t seq_len, int32_t 
            heads_q % heads_kv == 0 && d_qk >= 1 && d_v >= 1 && pattern_ok(p);
 }
 
-}  // namespace
-
-extern "C" {
-
-ssa_status ssa_prefill(ssa_dtype dtype, const void *q, const void *k, const void *v, void *o,
-                       float *lse, int32_t batch, int32_t seq_len, int32_t heads_q,
-                       int32_t heads_kv, int32_t d_qk, int32_t d_v, const int64_t q_strides[3],
-                       const int64_t k_strides[3], const int64_t v_strides[3],
-                       const int64_t o_strides[3], ssa_pattern pattern, float scale,
-                       hipStream_t stream) {
+// Checks shared by the prefill entry points and the argument block they
+// launch with. Returns SSA_OK with *empty set for a no-op call.
+ssa_status prefill_common(ssa_dtype dtype, const void *q, const void *k, const void *v, void *o,
+                          int32_t batch, int32_t seq_len, int32_t heads_q, int32_t heads_kv,
+                          int32_t d_qk, int32_t d_v, const int64_t q_strides[3],
+                          const int64_t k_strides[3], const int64_t v_strides[3],
+                          const int64_t o_strides[3], const ssa_pattern &pattern, float scale,
+                          PrefillArgs *a, bool *empty) {
+    *empty = false;
     if (!dtype_ok(dtype)) return SSA_ERR_INVALID_ARG;
     if (batch < 0 || seq_len < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv || d_qk < 1 ||
         d_v < 1)
@@ -223,7 +222,10 @@ ssa_status ssa_prefill(ssa_dtype dtype, const void *q, const void *k, const void
     if (!strides_ok(q_strides, 3, eb) || !strides_ok(k_strides, 3, eb) || !strides_ok(v_strides, 3, eb) ||
         !strides_ok(o_strides, 3, eb))
         return SSA_ERR_INVALID_ARG;
-    if (batch == 0 || seq_len == 0) return SSA_OK;
+    if (batch == 0 || seq_len == 0) {
+        *empty = true;
+        return SSA_OK;
+    }
     if (!q || !k || !v || !o) return SSA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SSA_ERR_INVALID_ARG;
     if (!ssa::prefill_supported(dtype == SSA_BF16, d_qk, d_v)) return SSA_ERR_UNSUPPORTED;
@@ -238,31 +240,78 @@ ssa_status ssa_prefill(ssa_dtype dtype, const void *q, const void *k, const void
     // a 1-D grid holds fewer than 2^32 work-items: 256 per work-group
     if (total >= (int64_t(1) << 24)) return SSA_ERR_UNSUPPORTED;
 
-    PrefillArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.lse = lse;
+    *a = PrefillArgs{};
+    a->q = q;
+    a->k = k;
+    a->v = v;
+    a->o = o;
     for (int i = 0; i < 3; ++i) {
-        a.qs[i] = q_strides[i];
-        a.ks[i] = k_strides[i];
-        a.vs[i] = v_strides[i];
-        a.os[i] = o_strides[i];
+        a->qs[i] = q_strides[i];
+        a->ks[i] = k_strides[i];
+        a->vs[i] = v_strides[i];
+        a->os[i] = o_strides[i];
     }
-    a.B = batch;
-    a.N = seq_len;
-    a.Hq = heads_q;
-    a.Hkv = heads_kv;
-    a.group = heads_q / heads_kv;
-    a.block = pattern.block;
-    a.sink = pattern.sink;
-    a.local = pattern.local;
-    a.scale_log2 = scale * 1.4426950408889634f;
-    a.num_qtiles = (int32_t)qtiles;
-    a.total_wgs = (int32_t)total;
+    a->B = batch;
+    a->N = seq_len;
+    a->Hq = heads_q;
+    a->Hkv = heads_kv;
+    a->group = heads_q / heads_kv;
+    a->block = pattern.block;
+    a->sink = pattern.sink;
+    a->local = pattern.local;
+    a->scale_log2 = scale * 1.4426950408889634f;
+    a->num_qtiles = (int32_t)qtiles;
+    a->total_wgs = (int32_t)total;
+    return SSA_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+ssa_status ssa_prefill(ssa_dtype dtype, const void *q, const void *k, const void *v, void *o,
+                       float *lse, int32_t batch, int32_t seq_len, int32_t heads_q,
+                       int32_t heads_kv, int32_t d_qk, int32_t d_v, const int64_t q_strides[3],
+                       const int64_t k_strides[3], const int64_t v_strides[3],
+                       const int64_t o_strides[3], ssa_pattern pattern, float scale,
+                       hipStream_t stream) {
+    PrefillArgs a;
+    bool empty;
+    const ssa_status st = prefill_common(dtype, q, k, v, o, batch, seq_len, heads_q, heads_kv, d_qk,
+                                         d_v, q_strides, k_strides, v_strides, o_strides, pattern,
+                                         scale, &a, &empty);
+    if (st != SSA_OK || empty) return st;
+    a.lse = lse;
     return ssa::launch_prefill(dtype == SSA_BF16, d_qk, d_v, a, stream) == hipSuccess ? SSA_OK
                                                                                      : SSA_ERR_HIP;
+}
+
+ssa_status ssa_prefill_dual(ssa_dtype dtype, const void *q, const void *k, const void *v,
+                            void *o_ssa, float *lse_ssa, void *o_full, float *lse_full, void *o_mix,
+                            float alpha, int32_t batch, int32_t seq_len, int32_t heads_q,
+                            int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                            const int64_t q_strides[3], const int64_t k_strides[3],
+                            const int64_t v_strides[3], const int64_t o_strides[3],
+                            ssa_pattern pattern, float scale, hipStream_t stream) {
+    if (!(alpha >= 0.f && alpha <= 1.f)) return SSA_ERR_INVALID_ARG;  // also rejects NaN
+    PrefillArgs a;
+    bool empty;
+    const ssa_status st = prefill_common(dtype, q, k, v, o_ssa, batch, seq_len, heads_q, heads_kv,
+                                         d_qk, d_v, q_strides, k_strides, v_strides, o_strides,
+                                         pattern, scale, &a, &empty);
+    if (st != SSA_OK || empty) return st;
+    if (!o_full || !aligned16(o_full) || (o_mix && !aligned16(o_mix))) return SSA_ERR_INVALID_ARG;
+    if (o_full == o_ssa || o_mix == o_ssa || o_mix == o_full) return SSA_ERR_INVALID_ARG;
+    if (!ssa::prefill_dual_supported(dtype == SSA_BF16, d_qk, d_v)) return SSA_ERR_UNSUPPORTED;
+    a.lse = lse_ssa;
+    a.o_full = o_full;
+    a.lse_full = lse_full;
+    a.o_mix = o_mix;
+    a.alpha = alpha;
+    return ssa::launch_prefill_dual(dtype == SSA_BF16, d_qk, d_v, a, stream) == hipSuccess
+               ? SSA_OK
+               : SSA_ERR_HIP;
 }
 
 ssa_status ssa_prefill_backward(ssa_dtype dtype, const void *q, const void *k, const void *v,

@@ -16,10 +16,19 @@ struct PrefillArgs {
     float scale_log2;        // softmax scale * log2(e)
     int32_t num_qtiles;      // ceil(N / 128)
     int32_t total_wgs;       // num_qtiles * Hq * B
+    // Dual mode (SSA and full causal attention in one pass): o / lse above
+    // receive the SSA result; these the full one and, if o_mix is set,
+    // alpha * o_full + (1 - alpha) * o (same strides as o).
+    void *o_full;
+    float *lse_full;         // [B, Hq, N] or null
+    void *o_mix;             // or null
+    float alpha;
 };
 
 bool prefill_supported(bool bf16, int d_qk, int d_v);
 hipError_t launch_prefill(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream);
+bool prefill_dual_supported(bool bf16, int d_qk, int d_v);
+hipError_t launch_prefill_dual(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream);
 
 // Backward of the prefill operator. Workspace: per (batch, query head, group
 // of 64 rows) the rows' lse * log2(e) then their D = sum_d dO*O (128 floats),

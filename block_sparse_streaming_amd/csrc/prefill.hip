@@ -60,7 +60,12 @@ __device__ __forceinline__ int v_swz(int row) {
     else return 4 * ((row >> 1) & 1);
 }
 
-template <int DQK, int DV>
+// DUAL: one pass yields both SSA attention and full causal attention. The
+// SSA sub-tiles come first, so the running state after the last of them is
+// the SSA result (written to o / lse); the walk then goes on over the keys SSA
+// leaves out, [min(s*b, q1), lo(q1-1)) with key j taken by row i iff j < lo(i),
+// and ends with full causal attention (o_full / lse_full, and the mix).
+template <int DQK, int DV, bool DUAL>
 __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArgs a) {
     constexpr int CK = DQK / 8, CV = DV / 8;   // 16-byte units per K / V row
     constexpr int NIK = CK / 4, NIV = CV / 4;  // direct transfers per wave per sub-tile
@@ -76,9 +81,20 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
     const int l32 = lane & 31, hi = lane >> 5;
 
-    const int wg = xcd_remap(blockIdx.x, a.total_wgs);
-    const int qt = wg % a.num_qtiles;
-    const int hb = wg / a.num_qtiles;
+    int qt, hb;
+    if constexpr (DUAL) {
+        // Full causal work grows with the tile index: dispatch the longest
+        // tiles first, all heads of one tile index together. Consecutive
+        // work-groups go to different XCDs, so when B * Hq is a multiple of 8
+        // every tile of a head runs on the same XCD (its L2).
+        const int per = a.total_wgs / a.num_qtiles;  // B * Hq
+        qt = a.num_qtiles - 1 - (int)blockIdx.x / per;
+        hb = (int)blockIdx.x % per;
+    } else {
+        const int wg = xcd_remap(blockIdx.x, a.total_wgs);
+        qt = wg % a.num_qtiles;
+        hb = wg / a.num_qtiles;
+    }
     const int h = hb % a.Hq, bb = hb / a.Hq;
     const int g = h / a.group;
 
@@ -132,8 +148,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             voff[n] = dma_off(p, CV, v_swz<CV>(p / CV), vs1, kBN);
         }
     }
-    auto issue = [&](int t, uint16_t *kb, uint16_t *vb) {
-        const SubTile st = sub_tile(tr, t);
+    auto issue = [&](int t, uint16_t *kb, uint16_t *vb) __attribute__((always_inline)) {
+        const SubTile st = sub_tile<DUAL>(tr, t);
         const int rows_valid = st.re - st.j0;
         const char *kt = (const char *)(kbase + (int64_t)st.j0 * a.ks[1]);
         const char *vt = (const char *)(vbase + (int64_t)st.j0 * a.vs[1]);
@@ -189,17 +205,28 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     const int r_last = r_first + 31 < a.N - 1 ? r_first + 31 : a.N - 1;
     const int lo_first_w = local_start(a, r_first), lo_last_w = local_start(a, r_last);
 
-    auto compute = [&](int t, const uint16_t *kb, const uint16_t *vb) {
-        const SubTile st = sub_tile(tr, t);
-        // What this sub-tile means for this wave's rows (wave-uniform): keys
-        // of a local sub-tile lie past the sink range, so there a key is
-        // attended iff lo_i <= j <= i; in the sink range iff j <= i.
-        const bool local = t >= tr.n_sink;
-        const int kend = st.j0 + kBN < st.re ? st.j0 + kBN : st.re;  // exclusive
-        if (r_first >= a.N || st.j0 > r_last || (local && kend <= lo_first_w)) return;  // nothing attended
-        const bool full = st.j0 + kBN <= st.re && (!local || st.j0 >= lo_last_w);
-        const bool no_mask = full && st.j0 + kBN - 1 <= r_first;  // every key <= every row
-        const bool causal_only = full && !no_mask;                // only j <= i can fail
+    auto compute = [&](int t, const uint16_t *kb, const uint16_t *vb) __attribute__((always_inline)) {
+        const SubTile st = sub_tile<DUAL>(tr, t);
+        bool no_mask, causal_only;
+        int edge = i;  // in a causal_only sub-tile, keys up to edge are attended
+        if (DUAL && t >= tr.n_total) {
+            // Complement sub-tile: key j (>= s*b) is attended iff j < lo_i,
+            // which also keeps out the re-read rows past the range end.
+            if (r_first >= a.N || st.j0 >= lo_last_w) return;
+            no_mask = st.j0 + kBN <= lo_first_w;
+            causal_only = !no_mask;
+            edge = lo_i - 1;
+        } else {
+            // What this sub-tile means for this wave's rows (wave-uniform):
+            // keys of a local sub-tile lie past the sink range, so there a key
+            // is attended iff lo_i <= j <= i; in the sink range iff j <= i.
+            const bool local = t >= tr.n_sink;
+            const int kend = st.j0 + kBN < st.re ? st.j0 + kBN : st.re;  // exclusive
+            if (r_first >= a.N || st.j0 > r_last || (local && kend <= lo_first_w)) return;  // nothing attended
+            const bool full = st.j0 + kBN <= st.re && (!local || st.j0 >= lo_last_w);
+            no_mask = full && st.j0 + kBN - 1 <= r_first;  // every key <= every row
+            causal_only = full && !no_mask;                // only j <= i can fail
+        }
         // Re-derive the lane offsets here (the empty asm hides their origin)
         // so that address arithmetic is not hoisted out of the loop into
         // registers that would stay live across it.
@@ -235,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         // is skipped. O and l always use the same m_run, so O / l is exact.
         float mx = -INFINITY;
         if (causal_only) {
-            const int d0 = i - (st.j0 + jl);  // key offset k is attended iff k <= d0
+            const int d0 = edge - (st.j0 + jl);  // key offset k is attended iff k <= d0
 #pragma unroll
             for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
@@ -311,55 +338,95 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         }
     };
 
+    // Writes O / l of the running state to `out` (row i) and its lse.
+    auto store_out = [&](void *out, float *lse_out) __attribute__((always_inline)) {
+        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        const float inv = 1.f / l_tot;
+        uint16_t *orow = (uint16_t *)out + bb * a.os[0] + (int64_t)i * a.os[1] + h * a.os[2];
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const u32x2 w{pack_bf16x2(oacc[d][4 * rq] * inv, oacc[d][4 * rq + 1] * inv),
+                              pack_bf16x2(oacc[d][4 * rq + 2] * inv, oacc[d][4 * rq + 3] * inv)};
+                if (row_ok) *(u32x2 *)(orow + d * 32 + 8 * rq + 4 * hi) = w;
+            }
+        if (row_ok && lse_out && hi == 0)
+            lse_out[((int64_t)bb * a.Hq + h) * a.N + i] = (m_run + log2f(l_tot)) * kLn2;
+    };
+    auto step = [&](int t, const uint16_t *kb, const uint16_t *vb) __attribute__((always_inline)) {
+        compute(t, kb, vb);
+        if constexpr (DUAL) {
+            if (t == tr.n_total - 1) store_out(a.o, a.lse);  // the SSA result
+        }
+    };
+
     // Two-stage pipeline: sub-tile t+1 streams into the other buffer while t
     // is computed. Buffers are separate LDS objects so the compiler can tell
     // the in-flight transfers from the buffer being read; the steady-state loop
     // issues and waits unconditionally and the last one or two sub-tiles are
     // peeled, so every wait is a fixed count.
-    const int T = tr.n_total;
+    const int T = DUAL ? tr.n_all : tr.n_total;
     int t = 0;
     if (T > 0) issue(0, k_buf0, v_buf0);
     for (; t + 2 < T; t += 2) {
         issue(t + 1, k_buf1, v_buf1);
         wait_vmcnt<NDMA>();
         barrier_no_fence();
-        compute(t, k_buf0, v_buf0);
+        step(t, k_buf0, v_buf0);
         barrier_lds_drained();
         issue(t + 2, k_buf0, v_buf0);
         wait_vmcnt<NDMA>();
         barrier_no_fence();
-        compute(t + 1, k_buf1, v_buf1);
+        step(t + 1, k_buf1, v_buf1);
         barrier_lds_drained();
     }
     if (t + 1 < T) {
         issue(t + 1, k_buf1, v_buf1);
         wait_vmcnt<NDMA>();
         barrier_no_fence();
-        compute(t, k_buf0, v_buf0);
+        step(t, k_buf0, v_buf0);
         wait_vmcnt<0>();
         barrier_no_fence();
-        compute(t + 1, k_buf1, v_buf1);
+        step(t + 1, k_buf1, v_buf1);
     } else if (t < T) {
         wait_vmcnt<0>();
         barrier_no_fence();
-        compute(t, k_buf0, v_buf0);
+        step(t, k_buf0, v_buf0);
     }
 
     // Epilogue: O = O / l, lse = ln 2 * (m + log2 l).
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.f / l_tot;
-    if (row_ok) {
-        uint16_t *orow = (uint16_t *)a.o + bb * a.os[0] + (int64_t)i * a.os[1] + h * a.os[2];
+    if constexpr (!DUAL) {
+        store_out(a.o, a.lse);
+    } else {
+        store_out(a.o_full, a.lse_full);
+        if (a.o_mix) {
+            // alpha * O_full + (1 - alpha) * O_ssa, from the fp32 full result
+            // and the rounded SSA result this lane stored earlier (a wave's
+            // accesses to one address stay in order; the opaque offset keeps
+            // the compiler from carrying the stored values in registers).
+            const float l_tot = l_run + __shfl_xor(l_run, 32);
+            const float wf = a.alpha / l_tot, ws = 1.f - a.alpha;
+            int64_t off = bb * a.os[0] + (int64_t)i * a.os[1] + h * a.os[2];
+            uint16_t *mrow = (uint16_t *)a.o_mix + off;
+            asm volatile("" : "+v"(off));
+            const uint16_t *srow = (const uint16_t *)a.o + off;
+            auto up = [](uint32_t w, int half) { return __uint_as_float(half ? w & 0xffff0000u : w << 16); };
+            if (row_ok) {
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
+                for (int d = 0; d < NDB; ++d)
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int col = d * 32 + 8 * rq + 4 * hi;
-                *(u32x2 *)(orow + col) =
-                    u32x2{pack_bf16x2(oacc[d][4 * rq] * inv, oacc[d][4 * rq + 1] * inv),
-                          pack_bf16x2(oacc[d][4 * rq + 2] * inv, oacc[d][4 * rq + 3] * inv)};
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const u32x2 sv = *(const u32x2 *)(srow + d * 32 + 8 * rq + 4 * hi);
+                        float m[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            m[e] = __builtin_fmaf(oacc[d][4 * rq + e], wf, ws * up(sv[e >> 1], e & 1));
+                        *(u32x2 *)(mrow + d * 32 + 8 * rq + 4 * hi) =
+                            u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])};
+                    }
             }
-        if (a.lse && hi == 0) a.lse[((int64_t)bb * a.Hq + h) * a.N + i] = (m_run + log2f(l_tot)) * kLn2;
+        }
     }
 }
 
@@ -511,12 +578,23 @@ bool prefill_supported(bool bf16, int d_qk, int d_v) {
 
 hipError_t launch_prefill(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream) {
     if (bf16) {
-        if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_bf16<64, 64>, a, stream);
-        if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_bf16<128, 128>, a, stream);
-        if (d_qk == 192 && d_v == 128) return launch(ssa_prefill_bf16<192, 128>, a, stream);
+        if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_bf16<64, 64, false>, a, stream);
+        if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_bf16<128, 128, false>, a, stream);
+        if (d_qk == 192 && d_v == 128) return launch(ssa_prefill_bf16<192, 128, false>, a, stream);
     } else {
         if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_f32<64, 64>, a, stream);
         if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_f32<128, 128>, a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+bool prefill_dual_supported(bool bf16, int d_qk, int d_v) { return bf16 && prefill_supported(true, d_qk, d_v); }
+
+hipError_t launch_prefill_dual(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream) {
+    if (bf16) {
+        if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_bf16<64, 64, true>, a, stream);
+        if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_bf16<128, 128, true>, a, stream);
+        if (d_qk == 192 && d_v == 128) return launch(ssa_prefill_bf16<192, 128, true>, a, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -29,6 +29,10 @@ __device__ __forceinline__ int local_start(const Args &a, int64_t q) {
 struct TileRanges {
     int q0, q1, sb, sink_end, loc_begin, lo_last;
     int n_sink, n_total;  // sub-tiles in the sink range, in both ranges
+    // The complement of the SSA keys within causal attention (full-attention
+    // mode only): keys [sink_end, gap_end) with j < lo(i) for row i, where
+    // gap_end = lo of the tile's last row. n_all counts all three ranges.
+    int gap_end, n_all;
 };
 
 template <class Args>
@@ -45,6 +49,8 @@ __device__ __forceinline__ TileRanges tile_ranges(const Args &a, int qt) {
     r.loc_begin = lo_first > r.sink_end ? lo_first : r.sink_end;
     r.n_sink = (r.sink_end + kBN - 1) / kBN;
     r.n_total = r.n_sink + (r.q1 - r.loc_begin + kBN - 1) / kBN;
+    r.gap_end = r.lo_last > r.sink_end ? r.lo_last : r.sink_end;
+    r.n_all = r.n_total + (r.gap_end - r.sink_end + kBN - 1) / kBN;
     return r;
 }
 
@@ -56,8 +62,18 @@ struct SubTile {
     bool need_mask;
 };
 
+// With GAP, sub-tiles n_total .. n_all-1 walk the complement range.
+template <bool GAP = false>
 __device__ __forceinline__ SubTile sub_tile(const TileRanges &r, int t) {
     SubTile s;
+    if constexpr (GAP) {
+        if (t >= r.n_total) {
+            s.j0 = r.sink_end + (t - r.n_total) * kBN;
+            s.re = r.gap_end;
+            s.need_mask = true;
+            return s;
+        }
+    }
     const bool local = t >= r.n_sink;
     s.j0 = local ? r.loc_begin + (t - r.n_sink) * kBN : t * kBN;
     s.re = local ? r.q1 : r.sink_end;

@@ -95,6 +95,40 @@ ssa_status ssa_prefill(ssa_dtype dtype, const void *q, const void *k, const void
                        hipStream_t stream);
 
 /*
+ * ssa_prefill_dual - SSA attention and full causal attention of the same
+ * q, k, v in one pass, plus their mix. The digest's calibration step (section
+ * 01, part (1): the calibration paragraph before the SSA paragraph) gives each
+ * attention module a learnable weight alpha in [0, 1] that mixes its full and
+ * sparse outputs; the equation was lost from the page, and the mix is read as
+ *     o_mix = alpha * o_full + (1 - alpha) * o_ssa.
+ * Calibration needs both outputs of every layer; SSA keys are a subset of the
+ * causal keys, so the kernel visits them first, writes the SSA result, and
+ * goes on over the remaining causal keys for the full result.
+ *
+ *   q, k, v        as in ssa_prefill.
+ *   o_ssa, lse_ssa what ssa_prefill writes (lse_ssa may be NULL).
+ *   o_full         full causal attention, softmax(scale q k^T) v over j <= i,
+ *                  [batch, seq_len, heads_q, d_v]; required.
+ *   lse_full       its lse [batch, heads_q, seq_len] fp32; may be NULL.
+ *   o_mix          alpha * o_full + (1 - alpha) * o_ssa, or NULL for none.
+ *                  It is formed from the fp32 full result and the rounded
+ *                  o_ssa already written.
+ *   o_strides      shared by o_ssa, o_full and o_mix, which must be distinct
+ *                  buffers that overlap neither each other nor the inputs.
+ *   alpha          in [0, 1] (checked even when o_mix is NULL).
+ * Cost is that of full causal attention (the SSA keys are not visited twice).
+ * batch == 0 or seq_len == 0 is a no-op. Compiled: bf16 with (d_qk, d_v) =
+ * (64,64), (128,128), (192,128); fp32 returns SSA_ERR_UNSUPPORTED.
+ */
+ssa_status ssa_prefill_dual(ssa_dtype dtype, const void *q, const void *k, const void *v,
+                            void *o_ssa, float *lse_ssa, void *o_full, float *lse_full, void *o_mix,
+                            float alpha, int32_t batch, int32_t seq_len, int32_t heads_q,
+                            int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                            const int64_t q_strides[3], const int64_t k_strides[3],
+                            const int64_t v_strides[3], const int64_t o_strides[3],
+                            ssa_pattern pattern, float scale, hipStream_t stream);
+
+/*
  * ssa_prefill_backward - gradients of ssa_prefill (same operator, same
  * pattern). The digest trains the sparsified layers further after replacing
  * them with SSA (section 01, part (1): the training paragraph after the SSA

@@ -123,6 +123,26 @@ def prefill(q, k, v, *, block=128, sink=1, local=7, scale, full=False, rows=None
     return o, lse, w
 
 
+def prefill_dual(q, k, v, *, block=128, sink=1, local=7, scale, alpha=None, rows=None):
+    """The calibration forward (LongCat ZigZag Attention digest, section 01
+    part (1), the calibration paragraph): SSA attention, full causal attention
+    and their mix, read as ``alpha * o_full + (1 - alpha) * o_ssa`` (the mix
+    equation is lost from the page).
+
+    Returns ``(o_ssa, lse_ssa, o_full, lse_full, o_mix)`` in float64, shapes as
+    ``prefill``; o_mix is None when ``alpha`` is None.
+    """
+    kw = dict(block=block, sink=sink, local=local, scale=scale, rows=rows)
+    o_ssa, lse_ssa, _ = prefill(q, k, v, **kw)
+    o_full, lse_full, _ = prefill(q, k, v, full=True, **kw)
+    o_mix = None
+    if alpha is not None:
+        if not 0.0 <= alpha <= 1.0:
+            raise ValueError("alpha must lie in [0, 1]")
+        o_mix = alpha * o_full + (1.0 - alpha) * o_ssa
+    return o_ssa, lse_ssa, o_full, lse_full, o_mix
+
+
 def decode_paged(q, k_cache, v_cache, page_table, ctx_lens, *, block=128, sink=1, local=7,
                  scale, full=False):
     """One new query per sequence against a paged cache.

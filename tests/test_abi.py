@@ -167,3 +167,29 @@ def test_backward_workspace_sizes():
         1 * 2 * 100 * 320 * 4
     assert ws(torch.float32, 1, 100, 2, 2, 128, 128) == 0    # not compiled
     assert ws(torch.bfloat16, 1, 100, 3, 2, 128, 128) == 0   # invalid heads
+
+
+def dual_call(dtype=1, B=1, N=256, Hq=4, Hkv=4, dqk=128, dv=128, pattern=(128, 1, 7), scale=0.1,
+              alpha=0.5, o_ssa=FAKE, o_full=FAKE + 0x1000, o_mix=FAKE + 0x2000):
+    lib = ssa.load_library()
+    st = strides(N * Hq * dqk, Hq * dqk, dqk)
+    p = ctypes.c_void_p(FAKE)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+    return lib.ssa_prefill_dual(dtype, p, p, p, vp(o_ssa), None, vp(o_full), None, vp(o_mix), alpha,
+                                B, N, Hq, Hkv, dqk, dv, st, st, st, st, ssa.Pattern(*pattern),
+                                scale, None)
+
+
+def test_dual_validation():
+    assert dual_call(alpha=-0.01) == INVALID
+    assert dual_call(alpha=1.01) == INVALID
+    assert dual_call(alpha=math.nan) == INVALID
+    assert dual_call(pattern=(128, 1, 0)) == INVALID
+    assert dual_call(scale=-1.0) == INVALID
+    assert dual_call(o_full=None) == INVALID               # the full output is required
+    assert dual_call(o_full=FAKE) == INVALID               # same buffer as o_ssa
+    assert dual_call(o_mix=FAKE + 0x1000) == INVALID       # same buffer as o_full
+    assert dual_call(o_full=FAKE + 0x1008) == INVALID      # misaligned
+    assert dual_call(dtype=0) == UNSUPPORTED                # fp32 has no dual kernel
+    assert dual_call(dqk=96, dv=96) == UNSUPPORTED
+    assert dual_call(N=0) == OK and dual_call(B=0) == OK   # no-op
