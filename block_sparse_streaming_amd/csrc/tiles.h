@@ -16,6 +16,12 @@ namespace ssa {
 constexpr int kBM = 128;  // query rows per work-group
 constexpr int kBN = 64;   // keys per sub-tile
 
+// By-value min / max. A conditional between two struct fields is an lvalue,
+// which clang lowers to a select of field addresses and can leave the struct
+// in scratch memory; these keep every select on values.
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+
 // First key of the local window of query position q, clamped to [0, N].
 // Args is any argument block with fields N, block, local.
 template <class Args>
@@ -42,14 +48,14 @@ __device__ __forceinline__ TileRanges tile_ranges(const Args &a, int qt) {
     const int64_t sb = (int64_t)a.sink * a.block;
     r.sb = (int)(sb < N ? sb : N);
     r.q0 = qt * kBM;
-    r.q1 = r.q0 + kBM < N ? r.q0 + kBM : N;
+    r.q1 = imin(r.q0 + kBM, N);
     const int lo_first = local_start(a, r.q0);
     r.lo_last = local_start(a, r.q1 - 1);
-    r.sink_end = r.sb < r.q1 ? r.sb : r.q1;
-    r.loc_begin = lo_first > r.sink_end ? lo_first : r.sink_end;
+    r.sink_end = imin(r.sb, r.q1);
+    r.loc_begin = imax(lo_first, r.sink_end);
     r.n_sink = (r.sink_end + kBN - 1) / kBN;
     r.n_total = r.n_sink + (r.q1 - r.loc_begin + kBN - 1) / kBN;
-    r.gap_end = r.lo_last > r.sink_end ? r.lo_last : r.sink_end;
+    r.gap_end = imax(r.lo_last, r.sink_end);
     r.n_all = r.n_total + (r.gap_end - r.sink_end + kBN - 1) / kBN;
     return r;
 }
@@ -68,15 +74,17 @@ __device__ __forceinline__ SubTile sub_tile(const TileRanges &r, int t) {
     SubTile s;
     if constexpr (GAP) {
         if (t >= r.n_total) {
+            // Uniform anyway; taken as a value (not a field load) so that the
+            // three-way choice of re stays a select of values.
             s.j0 = r.sink_end + (t - r.n_total) * kBN;
-            s.re = r.gap_end;
+            s.re = __builtin_amdgcn_readfirstlane(r.gap_end);
             s.need_mask = true;
             return s;
         }
     }
     const bool local = t >= r.n_sink;
     s.j0 = local ? r.loc_begin + (t - r.n_sink) * kBN : t * kBN;
-    s.re = local ? r.q1 : r.sink_end;
+    s.re = local ? (int)r.q1 : (int)r.sink_end;
     s.need_mask = !((s.j0 + kBN <= s.re) && (s.j0 + kBN - 1 <= r.q0) && (!local || s.j0 >= r.lo_last));
     return s;
 }
