@@ -9,14 +9,15 @@ and 256K tokens, SSA and full-attention decode on the 128K-context latent
 workload and SSA decode on the ragged 4K-1M workload (HBM GB/s of algorithmic
 bytes), the prefill backward at 32K and 256K tokens (TFLOP/s), the dual
 forward (SSA, full causal attention and their alpha-mix in one pass) at 32K
-(TFLOP/s of full causal attention), each against its roofline, and the CPU
-oracle timed on the prefill.
+(TFLOP/s of full causal attention), chunked prefill and multi-token decode
+against the paged cache (TFLOP/s; GB/s), each against its roofline, and the
+CPU oracle timed on the prefill.
 
 Inputs are synthetic (seeded N(0,1)) and resident in HBM before timing.
 Timing uses HIP events recorded on the stream the kernels are launched on
 (torch's current stream, which the binding passes to the library).
 
---profile {prefill,decode,backward,dual,copy} runs one short workload and prints nothing
+--profile {prefill,decode,backward,dual,extend,copy} runs one short workload and prints nothing
 else, for rocprofv3 counter collection (copy: a plain 1 GiB device copy whose
 counter readings calibrate FETCH_SIZE / WRITE_SIZE).
 """
@@ -175,7 +176,7 @@ def bench_prefill(cfg_id: int, steps: int, warmup: int):
     tflops = flops / (ms * 1e-3) / 1e12
     bf16 = cfg.dtype == torch.bfloat16
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
-    kernel = (f"ssa_prefill_bf16<{cfg.d_qk}, {cfg.d_v}, false>" if bf16 else
+    kernel = (f"ssa_prefill_bf16<{cfg.d_qk}, {cfg.d_v}, 0>" if bf16 else
               f"ssa_prefill_f32<{cfg.d_qk}, {cfg.d_v}>")
     grid = -(-cfg.N // 128) * cfg.Hq * cfg.B * 256
     res = {"workload": cfg.name, "ms": ms, "steps": steps, "algorithmic_flops": flops,
@@ -223,7 +224,7 @@ def bench_dual(cfg_id: int, steps: int, warmup: int):
     flops = cfg.N * (cfg.N + 1) // 2 * cfg.Hq * cfg.B * 2 * (cfg.d_qk + cfg.d_v)
     tflops = flops / (ms * 1e-3) / 1e12
     grid = -(-cfg.N // 128) * cfg.Hq * cfg.B * 256
-    kernel = f"ssa_prefill_bf16<{cfg.d_qk}, {cfg.d_v}, true>"
+    kernel = f"ssa_prefill_bf16<{cfg.d_qk}, {cfg.d_v}, 1>"
     name = cfg.name.replace("prefill", "prefill_dual", 1)
     res = {"workload": name, "ms": ms, "steps": steps, "algorithmic_flops": flops, "TFLOP/s": tflops,
            "alpha": DUAL_ALPHA,
@@ -231,6 +232,148 @@ def bench_dual(cfg_id: int, steps: int, warmup: int):
                                       "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                                       "traffic": recorded_traffic([f"{kernel} grid={grid}"])})}
     del step
+    free_gpu()
+    return name, res
+
+
+# ---------------------------------------------------------------------------
+# Extend: new tokens against the paged cache (chunked prefill, multi-token decode)
+# ---------------------------------------------------------------------------
+def extend_row_counts(lens, qlens, block: int, sink: int, local: int) -> np.ndarray:
+    """|A(p)| of every new row (position p = L - q_len + r), concatenated."""
+    out = []
+    sb = sink * block
+    for L, n in zip(lens, qlens):
+        p = np.arange(L - n, L, dtype=np.int64)
+        lo = np.maximum(sb, (p // block - local + 1) * block)
+        out.append(np.minimum(sb, p + 1) + np.maximum(0, p + 1 - lo))
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+def extend_union_tokens(L: int, n: int, block: int, sink: int, local: int) -> int:
+    """Cache rows some new row of a sequence attends: the sink blocks and
+    [lo(first new position), L)."""
+    sb = sink * block
+    p0 = L - n
+    lo = max(sb, (p0 // block - local + 1) * block)
+    return min(sb, L) + max(0, L - lo)
+
+
+def extend_chunk_setup():
+    import torch
+    import block_sparse_streaming_amd as ssa
+    from block_sparse_streaming_amd import inputs
+
+    lens, qlens = inputs.EXTEND_CHUNK_LENS, inputs.EXTEND_CHUNK_QLENS
+    inp = inputs.extend_inputs(lens, qlens, 16, 16, 128, 128, torch.bfloat16, "cuda:0",
+                               inputs.EXTEND_SEED)
+    out = torch.empty((sum(qlens), 16, 128), dtype=torch.bfloat16, device="cuda:0")
+    mq = max(qlens)
+
+    def step():
+        ssa.extend(inp.q, inp.k_cache, inp.v_cache, inp.page_table, inp.ctx_lens, inp.cu_q, mq,
+                   **inputs.PATTERN, out=out)
+
+    return inp, step
+
+
+def bench_extend_chunk(steps: int, warmup: int):
+    """ssa_extend on the chunked-prefill workload (paged tile kernel): four
+    sequences at 32K-128K tokens of context, each appending 8,192 tokens."""
+    import torch
+    from block_sparse_streaming_amd import inputs
+    inp, step = extend_chunk_setup()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_events(step, steps)
+    H, d = 16, 128
+    pairs = int(extend_row_counts(inp.lens, inp.qlens, **inputs.PATTERN).sum()) * H
+    flops = pairs * 2 * (d + d)
+    tflops = flops / (ms * 1e-3) / 1e12
+    grid = -(-max(inp.qlens) // 128) * H * len(inp.lens) * 256
+    name = "extend_chunk_bf16_b4_ctx32k-128k_q8192_h16_d128"
+    res = {"workload": name, "ms": ms, "steps": steps, "algorithmic_flops": flops, "TFLOP/s": tflops,
+           "roofline": with_measured({"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                                      "traffic": recorded_traffic(
+                                          [f"ssa_prefill_bf16<128, 128, 2> grid={grid}"])})}
+    del inp, step
+    free_gpu()
+    return name, res
+
+
+def extend_mtp_setup(n_inst: int):
+    """The multi-token decode workload, with n_inst page-table / query
+    instances over one cache (their selected pages together exceed the
+    Infinity Cache)."""
+    import torch
+    from block_sparse_streaming_amd import inputs
+    B, T = 32, inputs.EXTEND_MTP_Q
+    lens, qlens = (inputs.EXTEND_MTP_LEN,) * B, (T,) * B
+    base = inputs.extend_inputs(lens, qlens, 64, 1, 576, 512, torch.bfloat16, "cuda:0",
+                                inputs.EXTEND_MTP_SEED, latent=True)
+    insts = []
+    for r in range(n_inst):
+        table, _ = inputs.page_table_for(lens, inputs.PAGE_SIZE, seed=inputs.EXTEND_MTP_SEED + 100 + r)
+        g = inputs.generator("cuda:0", inputs.EXTEND_MTP_SEED + 200 + r)
+        qr = inputs.randn(tuple(base.q.shape), torch.bfloat16, "cuda:0", g)
+        insts.append((qr, torch.from_numpy(table).to("cuda:0")))
+    return base, insts
+
+
+def bench_extend_mtp(iters: int):
+    """ssa_extend on the multi-token decode workload (decode kernels over
+    query rows): 32 sequences at 128K tokens, four new tokens each, 64 query
+    heads on one 576-wide latent head. Rotates over 8 instances and replays a
+    HIP graph, as the latent decode measurement does."""
+    import torch
+    import block_sparse_streaming_amd as ssa
+    from block_sparse_streaming_amd import inputs
+    n_inst = 8
+    base, insts = extend_mtp_setup(n_inst)
+    B, T, Hq = len(base.lens), inputs.EXTEND_MTP_Q, 64
+    rows = B * T
+    max_pages = base.page_table.shape[1]
+    ws = torch.empty(max(16, ssa.extend_workspace_size(torch.bfloat16, B, rows, T, Hq, 1, 576, 512,
+                                                       inputs.PAGE_SIZE, max_pages, **inputs.PATTERN)),
+                     dtype=torch.uint8, device="cuda:0")
+    outs = [torch.empty((rows, Hq, 512), dtype=torch.bfloat16, device="cuda:0") for _ in range(n_inst)]
+
+    def call(r):
+        qr, tr = insts[r]
+        ssa.extend(qr, base.k_cache, base.v_cache, tr, base.ctx_lens, base.cu_q, T, **inputs.PATTERN,
+                   scale=576 ** -0.5, out=outs[r], workspace=ws)
+
+    for r in range(n_inst):
+        call(r)
+    torch.cuda.synchronize()
+    reps = 4
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for _ in range(reps):
+                for r in range(n_inst):
+                    call(r)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ms = time_events(graph.replay, max(1, iters // (reps * n_inst))) / (reps * n_inst)
+    # Algorithmic bytes: the union of the rows' attended latent rows (each read
+    # once), q and o, the page ids of those rows and the lengths.
+    union = [extend_union_tokens(L, T, **inputs.PATTERN) for L in base.lens]
+    nbytes = (sum(union) * 576 * 2 + rows * Hq * (576 + 512) * 2 +
+              sum(-(-u // inputs.PAGE_SIZE) for u in union) * 4 + (2 * B + 1) * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    name = "extend_mtp_bf16_latent_b32_q4_h64_d576_L131072"
+    res = {"workload": name, "us": ms * 1e3, "bytes": nbytes, "GB/s": gbs,
+           "rows_per_call": rows,
+           "roofline": decode_roofline(gbs, [f"decode_split_latent grid={8 * B * T * 256}",
+                                             f"decode_merge<true, 512> grid={rows * Hq * 64}"]),
+           "timing": f"HIP graph of {reps * n_inst} calls rotating over {n_inst} instances"}
+    del graph, insts, outs, base, ws
     free_gpu()
     return name, res
 
@@ -493,6 +636,11 @@ def profile_run(what: str):
         _, step = dual_setup(2)
         for _ in range(3):
             step()
+    elif what == "extend":
+        _, step = extend_chunk_setup()
+        for _ in range(3):
+            step()
+        bench_extend_mtp(32)
     elif what == "copy":
         n = 1 << 28                                   # 1 GiB of fp32 each way
         src = torch.ones(n, dtype=torch.float32, device="cuda:0")
@@ -507,7 +655,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--profile", choices=["prefill", "decode", "backward", "dual", "copy"], default=None)
+    ap.add_argument("--profile", choices=["prefill", "decode", "backward", "dual", "extend", "copy"], default=None)
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the 32K prefill (and the CPU oracle)")
     args = ap.parse_args()
@@ -555,6 +703,12 @@ def main():
         name, r = bench_dual(2, 10, 2)
         workloads[name] = r
         note(f"dual {name}: {r['ms']:.4f} ms/launch, {r['TFLOP/s']:.1f} TFLOP/s")
+        name, r = bench_extend_chunk(10, 2)
+        workloads[name] = r
+        note(f"extend {name}: {r['ms']:.4f} ms/call, {r['TFLOP/s']:.1f} TFLOP/s")
+        name, r = bench_extend_mtp(256)
+        workloads[name] = r
+        note(f"extend {name}: {r['us']:.2f} us/call ({r['GB/s']:.0f} GB/s)")
     cpu = cpu_baseline()
     note(f"cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
     from block_sparse_streaming_amd import inputs

@@ -21,7 +21,8 @@ SSA_BF16 = 1
 
 # Exported symbols, in the order include/ssa.h declares them.
 EXPORTS = ("ssa_prefill", "ssa_prefill_dual", "ssa_prefill_backward", "ssa_prefill_backward_workspace_size",
-           "ssa_decode", "full_attn_decode", "ssa_decode_workspace_size", "ssa_status_string")
+           "ssa_decode", "full_attn_decode", "ssa_decode_workspace_size", "ssa_extend",
+           "ssa_extend_workspace_size", "ssa_status_string")
 
 
 class SSAError(RuntimeError):
@@ -74,6 +75,12 @@ def load_library() -> ctypes.CDLL:
     lib.ssa_decode_workspace_size.restype = sz
     lib.ssa_decode_workspace_size.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32,
                                               Pattern, ctypes.c_int]
+    lib.ssa_extend.restype = ctypes.c_int
+    lib.ssa_extend.argtypes = [ctypes.c_int, p, p, p, i64p, i64p, p, i32, p, p, i32, i32, i32, i32, i32,
+                               i32, i32, i32, p, p, p, sz, Pattern, f32, p]
+    lib.ssa_extend_workspace_size.restype = sz
+    lib.ssa_extend_workspace_size.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, i32,
+                                              i32, Pattern]
     lib.ssa_status_string.restype = ctypes.c_char_p
     lib.ssa_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -309,3 +316,60 @@ def full_decode(q, k_cache, v_cache, page_table, ctx_lens, *, scale: float | Non
     """full_attn_decode: as ``decode`` but attending to the whole context."""
     return _decode(True, q, k_cache, v_cache, page_table, ctx_lens, block=1, sink=0, local=1,
                    scale=scale, out=out, workspace=workspace, return_lse=return_lse)
+
+
+def extend_workspace_size(dtype: torch.dtype, batch: int, total_q: int, max_q_len: int, heads_q: int,
+                          heads_kv: int, d_qk: int, d_v: int, page_size: int, max_pages: int, *,
+                          block: int = 128, sink: int = 1, local: int = 7) -> int:
+    """Bytes of workspace ssa_extend needs (0 for the tile kernel)."""
+    code = SSA_BF16 if dtype == torch.bfloat16 else SSA_F32
+    return int(load_library().ssa_extend_workspace_size(code, batch, total_q, max_q_len, heads_q,
+                                                        heads_kv, d_qk, d_v, page_size, max_pages,
+                                                        Pattern(block, sink, local)))
+
+
+def extend(q, k_cache, v_cache, page_table, ctx_lens, cu_q, max_q_len: int, *, block: int = 128,
+           sink: int = 1, local: int = 7, scale: float | None = None, out=None, workspace=None,
+           return_lse: bool = False):
+    """ssa_extend: q [total_q, Hq, d_qk] packed rows of the new tokens;
+    caches [pages, page_size, Hkv, d]; page_table [B, max_pages] int32;
+    ctx_lens [B] int32 (new tokens included); cu_q [B + 1] int32 prefix sums
+    of the chunk lengths; max_q_len bounds every chunk length."""
+    lib = load_library()
+    _on_gpu(q, k_cache, v_cache, page_table, ctx_lens, cu_q)
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    for t in (page_table, ctx_lens, cu_q):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError("page_table, ctx_lens and cu_q must be contiguous int32")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    total_q, Hq, d_qk = q.shape
+    _, page_size, Hkv, d_qk2 = k_cache.shape
+    d_v = v_cache.shape[3]
+    B = ctx_lens.shape[0]
+    if d_qk2 != d_qk or v_cache.shape[:3] != k_cache.shape[:3]:
+        raise ValueError("cache shape mismatch")
+    if page_table.dim() != 2 or page_table.shape[0] != B or cu_q.shape != (B + 1,):
+        raise ValueError("page_table must be [B, max_pages] and cu_q [B + 1]")
+    max_pages = page_table.shape[1]
+    if out is None:
+        out = torch.empty((total_q, Hq, d_v), dtype=q.dtype, device=q.device)
+    elif out.shape != (total_q, Hq, d_v) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [total_q, Hq, d_v] tensor of q's dtype")
+    lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    need = extend_workspace_size(q.dtype, B, total_q, max_q_len, Hq, Hkv, d_qk, d_v, page_size,
+                                 max_pages, block=block, sink=sink, local=local)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _on_gpu(workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.ssa_extend(dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _strides3(k_cache),
+                          _strides3(v_cache), _ptr(page_table), max_pages, _ptr(ctx_lens), _ptr(cu_q),
+                          B, total_q, int(max_q_len), Hq, Hkv, d_qk, d_v, page_size, _ptr(out),
+                          _ptr(lse), _ptr(workspace), ws_bytes, Pattern(block, sink, local),
+                          float(scale), _stream(q.device)))
+    return (out, lse) if return_lse else out

@@ -133,7 +133,7 @@ ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, co
     const WorkspaceLayout wl = workspace_layout(batch, heads_q, d_v, plan);
     if (!workspace || !aligned16(workspace) || workspace_bytes < wl.total) return SSA_ERR_WORKSPACE;
 
-    DecodeArgs a;
+    DecodeArgs a{};
     a.q = q;
     a.kc = k_cache;
     a.vc = v_cache;
@@ -265,6 +265,45 @@ ssa_status prefill_common(ssa_dtype dtype, const void *q, const void *k, const v
     return SSA_OK;
 }
 
+
+// Chunks up to this many rows per sequence go to the decode kernels (one
+// work-group per split of a row's window) when they support the shape; longer
+// ones to the paged tile kernel, which reads a window once per 128 rows.
+constexpr int32_t kExtendDecodeMaxRows = 8;
+
+struct ExtendPlan {
+    bool tiles;             // paged tile kernel, else decode kernels over query rows
+    DecodePlan dplan;       // decode path
+    size_t rows_bytes;      // decode path: row map (row_seq, row_ctx) at the workspace start
+    WorkspaceLayout wl;     // decode path: partials after the row map
+    size_t total;
+};
+
+bool extend_plan(ssa_dtype dtype, int32_t total_q, int32_t max_q_len, int32_t heads_q,
+                 int32_t heads_kv, int32_t d_qk, int32_t d_v, int32_t page_size, int32_t max_pages,
+                 const ssa_pattern &pattern, ExtendPlan *p) {
+    const bool tiles_ok = ssa::prefill_paged_supported(dtype == SSA_BF16, d_qk, d_v);
+    DecodePlan dp;
+    const bool dec_ok = make_plan(dtype, total_q, heads_q, heads_kv, d_qk, d_v, page_size, max_pages,
+                                  pattern, false, &dp);
+    if (!tiles_ok && !dec_ok) return false;
+    *p = ExtendPlan{};
+    p->tiles = tiles_ok && (!dec_ok || max_q_len > kExtendDecodeMaxRows);
+    if (p->tiles) return true;
+    p->dplan = dp;
+    p->rows_bytes = ((size_t)total_q * 2 * sizeof(int32_t) + 255) / 256 * 256;
+    p->wl = workspace_layout(total_q, heads_q, d_v, dp);
+    p->total = p->rows_bytes + p->wl.total;
+    return true;
+}
+
+bool extend_shape_ok(ssa_dtype dtype, int32_t batch, int32_t total_q, int32_t max_q_len,
+                     int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v, int32_t page_size,
+                     int32_t max_pages, const ssa_pattern &pattern) {
+    return dtype_ok(dtype) && batch >= 0 && total_q >= 0 && max_q_len >= 0 && heads_q >= 1 &&
+           heads_kv >= 1 && heads_q % heads_kv == 0 && d_qk >= 1 && d_v >= 1 && page_size >= 1 &&
+           max_pages >= 1 && pattern_ok(pattern) && (total_q == 0 || max_q_len >= 1);
+}
 
 }  // namespace
 
@@ -438,6 +477,133 @@ size_t ssa_decode_workspace_size(ssa_dtype dtype, int32_t batch, int32_t heads_q
                    &plan))
         return 0;
     return workspace_layout(batch, heads_q, d_v, plan).total;
+}
+
+ssa_status ssa_extend(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
+                      const int64_t k_strides[3], const int64_t v_strides[3],
+                      const int32_t *page_table, int32_t max_pages, const int32_t *ctx_lens,
+                      const int32_t *cu_q, int32_t batch, int32_t total_q, int32_t max_q_len,
+                      int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                      int32_t page_size, void *o, float *lse, void *workspace,
+                      size_t workspace_bytes, ssa_pattern pattern, float scale,
+                      hipStream_t stream) {
+    if (!extend_shape_ok(dtype, batch, total_q, max_q_len, heads_q, heads_kv, d_qk, d_v, page_size,
+                         max_pages, pattern))
+        return SSA_ERR_INVALID_ARG;
+    if (!(std::isfinite(scale) && scale > 0.f)) return SSA_ERR_INVALID_ARG;
+    const int eb = elem_bytes(dtype);
+    if (!strides_ok(k_strides, 3, eb) || !strides_ok(v_strides, 3, eb)) return SSA_ERR_INVALID_ARG;
+    if (batch == 0 || total_q == 0) return SSA_OK;
+    if (!q || !k_cache || !v_cache || !page_table || !ctx_lens || !cu_q || !o) return SSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+        return SSA_ERR_INVALID_ARG;
+    if ((d_qk * eb) % 16 || (d_v * eb) % 16) return SSA_ERR_INVALID_ARG;
+
+    ExtendPlan plan;
+    if (!extend_plan(dtype, total_q, max_q_len, heads_q, heads_kv, d_qk, d_v, page_size, max_pages,
+                     pattern, &plan))
+        return SSA_ERR_UNSUPPORTED;
+
+    if (plan.tiles) {
+        const int64_t qtiles = ((int64_t)max_q_len + 127) / 128;
+        const int64_t total = qtiles * heads_q * batch;
+        if (total >= (int64_t(1) << 24)) return SSA_ERR_UNSUPPORTED;
+        PrefillArgs a{};
+        a.q = q;
+        a.k = k_cache;
+        a.v = v_cache;
+        a.o = o;
+        a.lse = lse;
+        a.qs[0] = 0;
+        a.qs[1] = (int64_t)heads_q * d_qk;
+        a.qs[2] = d_qk;
+        a.os[0] = 0;
+        a.os[1] = (int64_t)heads_q * d_v;
+        a.os[2] = d_v;
+        for (int i = 0; i < 3; ++i) {
+            a.ks[i] = k_strides[i];
+            a.vs[i] = v_strides[i];
+        }
+        a.B = batch;
+        a.N = 0;
+        a.Hq = heads_q;
+        a.Hkv = heads_kv;
+        a.group = heads_q / heads_kv;
+        a.block = pattern.block;
+        a.sink = pattern.sink;
+        a.local = pattern.local;
+        a.scale_log2 = scale * 1.4426950408889634f;
+        a.num_qtiles = (int32_t)qtiles;
+        a.total_wgs = (int32_t)total;
+        a.page_table = page_table;
+        a.ctx_lens = ctx_lens;
+        a.cu_q = cu_q;
+        a.max_pages = max_pages;
+        a.page_size = page_size;
+        return ssa::launch_prefill_paged(dtype == SSA_BF16, d_qk, d_v, a, stream) == hipSuccess
+                   ? SSA_OK
+                   : SSA_ERR_HIP;
+    }
+
+    const DecodePlan &dp = plan.dplan;
+    if (dp.kind == ssa::kDecodeLatent &&
+        (v_cache != k_cache || v_strides[0] != k_strides[0] || v_strides[1] != k_strides[1] ||
+         v_strides[2] != k_strides[2]))
+        return SSA_ERR_UNSUPPORTED;
+    if ((int64_t)total_q * heads_q > kInt32Max || (int64_t)heads_kv * dp.head_chunks > 65535 ||
+        total_q > 65535 || heads_q > 65535 ||
+        (int64_t)dp.max_splits * heads_kv * dp.head_chunks * total_q > kInt32Max)
+        return SSA_ERR_UNSUPPORTED;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < plan.total) return SSA_ERR_WORKSPACE;
+
+    char *ws = static_cast<char *>(workspace);
+    int32_t *row_seq = reinterpret_cast<int32_t *>(ws);
+    int32_t *row_ctx = row_seq + total_q;
+    DecodeArgs a{};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    for (int i = 0; i < 3; ++i) {
+        a.ks[i] = k_strides[i];
+        a.vs[i] = v_strides[i];
+    }
+    a.page_table = page_table;
+    a.ctx_lens = ctx_lens;
+    a.max_pages = max_pages;
+    a.page_size = page_size;
+    a.B = total_q;
+    a.Hq = heads_q;
+    a.Hkv = heads_kv;
+    a.group = heads_q / heads_kv;
+    a.block = pattern.block;
+    a.sink = pattern.sink;
+    a.local = pattern.local;
+    a.full = 0;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.o = o;
+    a.lse = lse;
+    a.ws_o = reinterpret_cast<float *>(ws + plan.rows_bytes);
+    a.ws_lse = reinterpret_cast<float *>(ws + plan.rows_bytes + plan.wl.lse_offset);
+    a.plan = dp;
+    a.row_seq = row_seq;
+    a.row_ctx = row_ctx;
+    if (ssa::launch_extend_rows(cu_q, ctx_lens, batch, total_q, row_seq, row_ctx, stream) != hipSuccess)
+        return SSA_ERR_HIP;
+    return ssa::launch_decode(dtype == SSA_BF16, d_qk, d_v, a, stream) == hipSuccess ? SSA_OK : SSA_ERR_HIP;
+}
+
+size_t ssa_extend_workspace_size(ssa_dtype dtype, int32_t batch, int32_t total_q, int32_t max_q_len,
+                                 int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                                 int32_t page_size, int32_t max_pages, ssa_pattern pattern) {
+    if (!extend_shape_ok(dtype, batch, total_q, max_q_len, heads_q, heads_kv, d_qk, d_v, page_size,
+                         max_pages, pattern) ||
+        batch == 0 || total_q == 0)
+        return 0;
+    ExtendPlan plan;
+    if (!extend_plan(dtype, total_q, max_q_len, heads_q, heads_kv, d_qk, d_v, page_size, max_pages,
+                     pattern, &plan))
+        return 0;
+    return plan.total;
 }
 
 const char *ssa_status_string(ssa_status status) {

@@ -43,6 +43,14 @@ struct Sel {
     int64_t total;     // |R1| + |R2|
 };
 
+// Context length (query position + 1) and page-table row of query row r.
+__device__ __forceinline__ int64_t row_context(const DecodeArgs &a, int r) {
+    return a.row_ctx ? (int64_t)a.row_ctx[r] : (int64_t)a.ctx_lens[r];
+}
+__device__ __forceinline__ int64_t row_sequence(const DecodeArgs &a, int r) {
+    return a.row_seq ? (int64_t)a.row_seq[r] : (int64_t)r;
+}
+
 __device__ __forceinline__ Sel select_tokens(int64_t L, const DecodeArgs &a) {
     if (a.full) return Sel{L, L, L};
     const int64_t b = a.block, sb = (int64_t)a.sink * b;
@@ -111,7 +119,7 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
 
     const int split = blockIdx.x, g = blockIdx.y, bb = blockIdx.z;
     const int tid = threadIdx.x, tg = tid / kTpt, tl = tid % kTpt;
-    const int64_t L = a.ctx_lens[bb];
+    const int64_t L = row_context(a, bb);
     if (L <= 0) return;
     const Sel sel = select_tokens(L, a);
     const int64_t p_begin = (int64_t)split * a.plan.split_tokens;
@@ -121,7 +129,7 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
     // Positions and tokens fit in 32 bits (context lengths are int32).
     const uint32_t up_end = (uint32_t)p_end, ur1 = (uint32_t)sel.r1_end, ur2 = (uint32_t)sel.r2_begin;
     const uint32_t uP = (uint32_t)a.page_size;
-    const int32_t *ptab = a.page_table + (int64_t)bb * a.max_pages;
+    const int32_t *ptab = a.page_table + row_sequence(a, bb) * a.max_pages;
 
     // Token of lane group tg's u-th position in the chunk starting at c0
     // (clamped to the split's last position; masked later).
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, kg = lane >> 4;
 
-    const int64_t L = a.ctx_lens[bb];
+    const int64_t L = row_context(a, bb);
     if (L <= 0) return;
     const Sel sel = select_tokens(L, a);
     const int64_t p_begin = (int64_t)split * a.plan.split_tokens;
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     const int64_t lp2 = t2 / P;
     const int n2 = p_end > s2 ? (int)((sel.r2_begin + (p_end - sel.r1_end) - 1) / P - lp2 + 1) : 0;
     for (int t = tid; t < n1 + n2; t += kLatThreads)
-        pids[t] = a.page_table[(int64_t)bb * a.max_pages + (t < n1 ? lp1 + t : lp2 + (t - n1))];
+        pids[t] = a.page_table[row_sequence(a, bb) * a.max_pages + (t < n1 ? lp1 + t : lp2 + (t - n1))];
 
     const int heads_here = a.group - hc * 64 < 64 ? a.group - hc * 64 : 64;
     const bool active = wave * 16 < heads_here;
@@ -520,7 +528,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
     const int row = blockIdx.x * (kMergeThreads / 64) + (threadIdx.x >> 6);  // bb * Hq + h
     if (row >= a.B * a.Hq) return;
     const int bb = row / a.Hq;
-    const int64_t L = a.ctx_lens[bb];
+    const int64_t L = row_context(a, bb);
     Elem *out = (Elem *)a.o + (int64_t)row * D + E * lane;
     int ns = 0;
     if (L > 0) {
@@ -634,6 +642,27 @@ hipError_t launch_valu_d(int d, const DecodeArgs &a, hipStream_t stream) {
     }
 }
 
+
+// One thread per packed query row: its sequence (the last b with
+// cu_q[b] <= r, by binary search) and its context length. The length is
+// clamped to the sequence's, so malformed prefix sums stay within the cache.
+__global__ __launch_bounds__(256) void extend_rows(const int32_t *cu_q, const int32_t *ctx_lens,
+                                                   int32_t batch, int32_t total_q, int32_t *row_seq,
+                                                   int32_t *row_ctx) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= total_q) return;
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu_q[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    const int ctx = ctx_lens[lo];
+    const int v = ctx - (cu_q[lo + 1] - 1 - r);
+    row_seq[r] = lo;
+    row_ctx[r] = v < ctx ? v : ctx;
+}
+
 }  // namespace
 
 bool decode_valu_supported(bool bf16, int d_qk, int d_v, int group) {
@@ -671,6 +700,13 @@ hipError_t launch_decode(bool bf16, int d_qk, int d_v, const DecodeArgs &a, hipS
     const int rows_per_wg = kMergeThreads / 64;
     const int64_t wgs = ((int64_t)a.B * a.Hq + rows_per_wg - 1) / rows_per_wg;
     return hipLaunchKernel(merge, dim3((unsigned)wgs), dim3(kMergeThreads), margs, 0, stream);
+}
+
+hipError_t launch_extend_rows(const int32_t *cu_q, const int32_t *ctx_lens, int32_t batch,
+                              int32_t total_q, int32_t *row_seq, int32_t *row_ctx, hipStream_t stream) {
+    void *args[] = {(void *)&cu_q, (void *)&ctx_lens, (void *)&batch, (void *)&total_q, (void *)&row_seq,
+                    (void *)&row_ctx};
+    return hipLaunchKernel((const void *)extend_rows, dim3((total_q + 255) / 256), dim3(256), args, 0, stream);
 }
 
 }  // namespace ssa

@@ -23,12 +23,26 @@ struct PrefillArgs {
     float *lse_full;         // [B, Hq, N] or null
     void *o_mix;             // or null
     float alpha;
+    // Paged mode (new tokens of each sequence against a paged cache): q / o
+    // are packed rows [total_q, Hq, d] (qs[0] = os[0] = 0), k / v are the
+    // caches with (page, slot, head) strides, and sequence b's rows
+    // cu_q[b] .. cu_q[b+1]-1 sit at the last positions of its ctx_lens[b]
+    // tokens. num_qtiles is then the tiles of the longest chunk; lse is
+    // [total_q, Hq].
+    const int32_t *page_table;  // [B, max_pages]
+    const int32_t *ctx_lens;    // [B]
+    const int32_t *cu_q;        // [B + 1]
+    int32_t max_pages, page_size;
 };
+
+enum PrefillMode { kModePlain = 0, kModeDual = 1, kModePaged = 2 };
 
 bool prefill_supported(bool bf16, int d_qk, int d_v);
 hipError_t launch_prefill(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream);
 bool prefill_dual_supported(bool bf16, int d_qk, int d_v);
 hipError_t launch_prefill_dual(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream);
+bool prefill_paged_supported(bool bf16, int d_qk, int d_v);
+hipError_t launch_prefill_paged(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream);
 
 // Backward of the prefill operator. Workspace: per (batch, query head, group
 // of 64 rows) the rows' lse * log2(e) then their D = sum_d dO*O (128 floats),
@@ -86,10 +100,20 @@ struct DecodeArgs {
     float *ws_o;                    // [B, Hq, max_splits, d_v]
     float *ws_lse;                  // [B, Hq, max_splits], log2 domain
     DecodePlan plan;
+    // Several query rows per sequence: B counts query rows, and row r reads
+    // page-table row row_seq[r] with context length row_ctx[r] (its position
+    // + 1). Null for one row per sequence (row r = sequence r, ctx_lens[r]).
+    const int32_t *row_seq;
+    const int32_t *row_ctx;
 };
 
 bool decode_valu_supported(bool bf16, int d_qk, int d_v, int group);
 bool decode_latent_supported(bool bf16, int d_qk, int d_v, int group);
 hipError_t launch_decode(bool bf16, int d_qk, int d_v, const DecodeArgs &a, hipStream_t stream);
+
+// Row map of packed query rows: row r of sequence b (cu_q[b] <= r < cu_q[b+1])
+// gets row_seq[r] = b and row_ctx[r] = ctx_lens[b] - (cu_q[b+1] - 1 - r).
+hipError_t launch_extend_rows(const int32_t *cu_q, const int32_t *ctx_lens, int32_t batch,
+                              int32_t total_q, int32_t *row_seq, int32_t *row_ctx, hipStream_t stream);
 
 }  // namespace ssa

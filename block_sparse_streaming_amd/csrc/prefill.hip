@@ -60,16 +60,26 @@ __device__ __forceinline__ int v_swz(int row) {
     else return 4 * ((row >> 1) & 1);
 }
 
-// DUAL: one pass yields both SSA attention and full causal attention. The
-// SSA sub-tiles come first, so the running state after the last of them is
-// the SSA result (written to o / lse); the walk then goes on over the keys SSA
-// leaves out, [min(s*b, q1), lo(q1-1)) with key j taken by row i iff j < lo(i),
-// and ends with full causal attention (o_full / lse_full, and the mix).
-template <int DQK, int DV, bool DUAL>
+// MODE kModeDual: one pass yields both SSA attention and full causal
+// attention. The SSA sub-tiles come first, so the running state after the
+// last of them is the SSA result (written to o / lse); the walk then goes on
+// over the keys SSA leaves out, [min(s*b, q1), lo(q1-1)) with key j taken by
+// row i iff j < lo(i), and ends with full causal attention (o_full / lse_full,
+// and the mix).
+// MODE kModePaged: the new tokens of each sequence (a prefill chunk, or a few
+// decode tokens) against a paged cache. A tile is 128 consecutive new rows of
+// one sequence, at the last positions of its context; every key row is found
+// through the page table (page ids of the next sub-tile are read one stage
+// ahead, one per lane, and shared with ds_bpermute).
+template <int DQK, int DV, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArgs a) {
+    constexpr bool DUAL = MODE == kModeDual, PAGED = MODE == kModePaged;
     constexpr int CK = DQK / 8, CV = DV / 8;   // 16-byte units per K / V row
     constexpr int NIK = CK / 4, NIV = CV / 4;  // direct transfers per wave per sub-tile
     constexpr int NDMA = NIK + NIV;
+    // Memory operations a stage leaves in flight: its transfers, plus in
+    // paged mode the page-id read of the stage after it.
+    constexpr int NW = NDMA + (PAGED ? 1 : 0);
     constexpr int NQ = DQK / 16, NDB = DV / 32;
     static_assert(CK % 4 == 0 && CV % 4 == 0, "tile rows must split into whole waves");
     __shared__ __attribute__((aligned(1024))) uint16_t k_buf0[kBN * DQK];
@@ -98,20 +108,41 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     const int h = hb % a.Hq, bb = hb / a.Hq;
     const int g = h / a.group;
 
-    const TileRanges tr = tile_ranges(a, qt);
-    const int i = tr.q0 + wave * 32 + l32;  // this lane's query row
-    const bool row_ok = i < a.N;
-    const int lo_i = local_start(a, i);
+    // Sequence geometry. Paged: the chunk's rows [0, q_len) sit at positions
+    // pos0 .. pos0 + q_len - 1 of a context of ctx tokens; row r of the chunk
+    // is packed row q_start + r of q and o. Plain: the whole sequence.
+    Geo geo = geo_of(a);
+    int pos0 = 0, q_start = 0, q0, q1;
+    if constexpr (PAGED) {
+        q_start = a.cu_q[bb];
+        const int q_len = a.cu_q[bb + 1] - q_start;
+        if (qt * kBM >= q_len) return;  // this sequence has fewer tiles (uniform)
+        geo.N = a.ctx_lens[bb];
+        pos0 = geo.N - q_len;
+        pos0 = pos0 > 0 ? pos0 : 0;     // q_len <= ctx is a precondition; stay in bounds
+        q0 = pos0 + qt * kBM;
+        q1 = imin(pos0 + imin(q_len, qt * kBM + kBM), geo.N);
+    } else {
+        q0 = qt * kBM;
+        q1 = imin(q0 + kBM, a.N);
+    }
+    const TileRanges tr = tile_ranges_at(geo, q0, q1);
+    const int n_end = PAGED ? q1 : a.N;     // rows at positions >= n_end are not computed
+    const int i = tr.q0 + wave * 32 + l32;  // this lane's query row (its position)
+    const bool row_ok = i < n_end;
+    const int lo_i = local_start(geo, i);
+    // Index of row i along the token axis of q / o (packed rows when paged).
+    const int64_t row_idx = PAGED ? (int64_t)q_start + (i - pos0) : (int64_t)i;
 
     const uint16_t *qbase = (const uint16_t *)a.q + bb * a.qs[0] + h * a.qs[2];
-    const uint16_t *kbase = (const uint16_t *)a.k + bb * a.ks[0] + g * a.ks[2];
-    const uint16_t *vbase = (const uint16_t *)a.v + bb * a.vs[0] + g * a.vs[2];
+    const uint16_t *kbase = (const uint16_t *)a.k + (PAGED ? 0 : bb * a.ks[0]) + g * a.ks[2];
+    const uint16_t *vbase = (const uint16_t *)a.v + (PAGED ? 0 : bb * a.vs[0]) + g * a.vs[2];
     const int ks1 = (int)a.ks[1], vs1 = (int)a.vs[1];  // token strides (< 2^24, host-checked)
 
     // Q^T operand, resident in registers for the whole tile.
     bf16x8 qf[NQ];
     {
-        const uint16_t *qrow = qbase + (int64_t)i * a.qs[1] + 8 * hi;
+        const uint16_t *qrow = qbase + row_idx * a.qs[1] + 8 * hi;
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks) {
             u32x4 w = {0u, 0u, 0u, 0u};
@@ -148,7 +179,46 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             voff[n] = dma_off(p, CV, v_swz<CV>(p / CV), vs1, kBN);
         }
     }
+    // Paged mode: lane l holds the page and slot of key row l of the next
+    // sub-tile to be issued (rows past the range end take its last row).
+    const int32_t *ptab = PAGED ? a.page_table + (int64_t)bb * a.max_pages : nullptr;
+    int pg_next = 0, sl_next = 0;
+    auto read_ids = [&](int t) __attribute__((always_inline)) {
+        const SubTile st = sub_tile<false>(tr, t);
+        const int tok = st.j0 + imin(lane, st.re - st.j0 - 1);
+        const int lp = tok / a.page_size;
+        sl_next = tok - lp * a.page_size;
+        pg_next = ptab[lp];
+    };
+    auto issue_paged = [&](int t, uint16_t *kb, uint16_t *vb) __attribute__((always_inline)) {
+        const SubTile st = sub_tile<false>(tr, t);
+        const int rows_valid = st.re - st.j0;
+        const int pg = pg_next, sl = sl_next;
+        // Read the next stage's ids before this stage's transfers, so that the
+        // transfers stay the youngest operations in flight. The last stage
+        // re-reads its own ids, which keeps the count fixed.
+        read_ids(imin(t + 1, tr.n_total - 1));
+        auto src = [&](int p, int C, int swz, int64_t s0, int64_t s1) __attribute__((always_inline)) {
+            const int row = imin(p / C, rows_valid - 1);
+            const int64_t page = __shfl(pg, row), slot = __shfl(sl, row);
+            return page * s0 + slot * s1 + (((p % C) ^ swz) * 8);
+        };
+#pragma unroll
+        for (int n = 0; n < NIK; ++n) {
+            const int p = (wave * NIK + n) * 64 + lane;
+            dma16(kbase + src(p, CK, k_swz<CK>(p / CK), a.ks[0], a.ks[1]), kb + (wave * NIK + n) * 512);
+        }
+#pragma unroll
+        for (int n = 0; n < NIV; ++n) {
+            const int p = (wave * NIV + n) * 64 + lane;
+            dma16(vbase + src(p, CV, v_swz<CV>(p / CV), a.vs[0], a.vs[1]), vb + (wave * NIV + n) * 512);
+        }
+    };
     auto issue = [&](int t, uint16_t *kb, uint16_t *vb) __attribute__((always_inline)) {
+        if constexpr (PAGED) {
+            issue_paged(t, kb, vb);
+            return;
+        }
         const SubTile st = sub_tile<DUAL>(tr, t);
         const int rows_valid = st.re - st.j0;
         const char *kt = (const char *)(kbase + (int64_t)st.j0 * a.ks[1]);
@@ -202,8 +272,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     // Rows of this wave: r_first .. r_last (clamped to the sequence), and the
     // window starts of its first and last rows.
     const int r_first = tr.q0 + wave * 32;
-    const int r_last = r_first + 31 < a.N - 1 ? r_first + 31 : a.N - 1;
-    const int lo_first_w = local_start(a, r_first), lo_last_w = local_start(a, r_last);
+    const int r_last = r_first + 31 < n_end - 1 ? r_first + 31 : n_end - 1;
+    const int lo_first_w = local_start(geo, r_first), lo_last_w = local_start(geo, r_last);
 
     auto compute = [&](int t, const uint16_t *kb, const uint16_t *vb) __attribute__((always_inline)) {
         const SubTile st = sub_tile<DUAL>(tr, t);
@@ -212,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         if (DUAL && t >= tr.n_total) {
             // Complement sub-tile: key j (>= s*b) is attended iff j < lo_i,
             // which also keeps out the re-read rows past the range end.
-            if (r_first >= a.N || st.j0 >= lo_last_w) return;
+            if (r_first >= n_end || st.j0 >= lo_last_w) return;
             no_mask = st.j0 + kBN <= lo_first_w;
             causal_only = !no_mask;
             edge = lo_i - 1;
@@ -222,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             // is attended iff lo_i <= j <= i; in the sink range iff j <= i.
             const bool local = t >= tr.n_sink;
             const int kend = st.j0 + kBN < st.re ? st.j0 + kBN : st.re;  // exclusive
-            if (r_first >= a.N || st.j0 > r_last || (local && kend <= lo_first_w)) return;  // nothing attended
+            if (r_first >= n_end || st.j0 > r_last || (local && kend <= lo_first_w)) return;  // nothing attended
             const bool full = st.j0 + kBN <= st.re && (!local || st.j0 >= lo_last_w);
             no_mask = full && st.j0 + kBN - 1 <= r_first;  // every key <= every row
             causal_only = full && !no_mask;                // only j <= i can fail
@@ -342,7 +412,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     auto store_out = [&](void *out, float *lse_out) __attribute__((always_inline)) {
         const float l_tot = l_run + __shfl_xor(l_run, 32);
         const float inv = 1.f / l_tot;
-        uint16_t *orow = (uint16_t *)out + bb * a.os[0] + (int64_t)i * a.os[1] + h * a.os[2];
+        uint16_t *orow = (uint16_t *)out + bb * a.os[0] + row_idx * a.os[1] + h * a.os[2];
 #pragma unroll
         for (int d = 0; d < NDB; ++d)
 #pragma unroll
@@ -351,8 +421,10 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
                               pack_bf16x2(oacc[d][4 * rq + 2] * inv, oacc[d][4 * rq + 3] * inv)};
                 if (row_ok) *(u32x2 *)(orow + d * 32 + 8 * rq + 4 * hi) = w;
             }
-        if (row_ok && lse_out && hi == 0)
-            lse_out[((int64_t)bb * a.Hq + h) * a.N + i] = (m_run + log2f(l_tot)) * kLn2;
+        if (row_ok && lse_out && hi == 0) {
+            const int64_t li = PAGED ? row_idx * a.Hq + h : ((int64_t)bb * a.Hq + h) * a.N + i;
+            lse_out[li] = (m_run + log2f(l_tot)) * kLn2;
+        }
     };
     auto step = [&](int t, const uint16_t *kb, const uint16_t *vb) __attribute__((always_inline)) {
         compute(t, kb, vb);
@@ -368,22 +440,25 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     // peeled, so every wait is a fixed count.
     const int T = DUAL ? tr.n_all : tr.n_total;
     int t = 0;
-    if (T > 0) issue(0, k_buf0, v_buf0);
+    if (T > 0) {
+        if constexpr (PAGED) read_ids(0);
+        issue(0, k_buf0, v_buf0);
+    }
     for (; t + 2 < T; t += 2) {
         issue(t + 1, k_buf1, v_buf1);
-        wait_vmcnt<NDMA>();
+        wait_vmcnt<NW>();
         barrier_no_fence();
         step(t, k_buf0, v_buf0);
         barrier_lds_drained();
         issue(t + 2, k_buf0, v_buf0);
-        wait_vmcnt<NDMA>();
+        wait_vmcnt<NW>();
         barrier_no_fence();
         step(t + 1, k_buf1, v_buf1);
         barrier_lds_drained();
     }
     if (t + 1 < T) {
         issue(t + 1, k_buf1, v_buf1);
-        wait_vmcnt<NDMA>();
+        wait_vmcnt<NW>();
         barrier_no_fence();
         step(t, k_buf0, v_buf0);
         wait_vmcnt<0>();
@@ -578,9 +653,9 @@ bool prefill_supported(bool bf16, int d_qk, int d_v) {
 
 hipError_t launch_prefill(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream) {
     if (bf16) {
-        if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_bf16<64, 64, false>, a, stream);
-        if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_bf16<128, 128, false>, a, stream);
-        if (d_qk == 192 && d_v == 128) return launch(ssa_prefill_bf16<192, 128, false>, a, stream);
+        if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_bf16<64, 64, kModePlain>, a, stream);
+        if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_bf16<128, 128, kModePlain>, a, stream);
+        if (d_qk == 192 && d_v == 128) return launch(ssa_prefill_bf16<192, 128, kModePlain>, a, stream);
     } else {
         if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_f32<64, 64>, a, stream);
         if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_f32<128, 128>, a, stream);
@@ -592,9 +667,20 @@ bool prefill_dual_supported(bool bf16, int d_qk, int d_v) { return bf16 && prefi
 
 hipError_t launch_prefill_dual(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream) {
     if (bf16) {
-        if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_bf16<64, 64, true>, a, stream);
-        if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_bf16<128, 128, true>, a, stream);
-        if (d_qk == 192 && d_v == 128) return launch(ssa_prefill_bf16<192, 128, true>, a, stream);
+        if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_bf16<64, 64, kModeDual>, a, stream);
+        if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_bf16<128, 128, kModeDual>, a, stream);
+        if (d_qk == 192 && d_v == 128) return launch(ssa_prefill_bf16<192, 128, kModeDual>, a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+bool prefill_paged_supported(bool bf16, int d_qk, int d_v) { return bf16 && prefill_supported(true, d_qk, d_v); }
+
+hipError_t launch_prefill_paged(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hipStream_t stream) {
+    if (bf16) {
+        if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_bf16<64, 64, kModePaged>, a, stream);
+        if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_bf16<128, 128, kModePaged>, a, stream);
+        if (d_qk == 192 && d_v == 128) return launch(ssa_prefill_bf16<192, 128, kModePaged>, a, stream);
     }
     return hipErrorInvalidValue;
 }

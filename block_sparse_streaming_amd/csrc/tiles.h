@@ -41,16 +41,26 @@ struct TileRanges {
     int gap_end, n_all;
 };
 
+// The pattern and the sequence length a tile's ranges are computed against.
+struct Geo {
+    int N, block, sink, local;
+};
+
 template <class Args>
-__device__ __forceinline__ TileRanges tile_ranges(const Args &a, int qt) {
+__device__ __forceinline__ Geo geo_of(const Args &a) {
+    return Geo{a.N, a.block, a.sink, a.local};
+}
+
+// Ranges of the rows at positions [q0, q1) of a sequence of length g.N.
+__device__ __forceinline__ TileRanges tile_ranges_at(const Geo &g, int q0, int q1) {
     TileRanges r;
-    const int N = a.N;
-    const int64_t sb = (int64_t)a.sink * a.block;
+    const int N = g.N;
+    const int64_t sb = (int64_t)g.sink * g.block;
     r.sb = (int)(sb < N ? sb : N);
-    r.q0 = qt * kBM;
-    r.q1 = imin(r.q0 + kBM, N);
-    const int lo_first = local_start(a, r.q0);
-    r.lo_last = local_start(a, r.q1 - 1);
+    r.q0 = q0;
+    r.q1 = q1;
+    const int lo_first = local_start(g, r.q0);
+    r.lo_last = local_start(g, r.q1 - 1);
     r.sink_end = imin(r.sb, r.q1);
     r.loc_begin = imax(lo_first, r.sink_end);
     r.n_sink = (r.sink_end + kBN - 1) / kBN;
@@ -58,6 +68,12 @@ __device__ __forceinline__ TileRanges tile_ranges(const Args &a, int qt) {
     r.gap_end = imax(r.lo_last, r.sink_end);
     r.n_all = r.n_total + (r.gap_end - r.sink_end + kBN - 1) / kBN;
     return r;
+}
+
+// Query tile qt (rows [128 qt, 128 qt + 128) clamped to a.N) of a whole sequence.
+template <class Args>
+__device__ __forceinline__ TileRanges tile_ranges(const Args &a, int qt) {
+    return tile_ranges_at(geo_of(a), qt * kBM, imin(qt * kBM + kBM, a.N));
 }
 
 // Sub-tile t of a tile: first key, end of its range, and whether any pair in

@@ -156,6 +156,49 @@ def decode_inputs(cfg: DecodeConfig, device, *, lens=None, seed: int | None = No
                         torch.tensor(lens, dtype=torch.int32, device=device), table, lens)
 
 
+# Chunked prefill workload: four sequences with 32K-128K tokens of context,
+# each appending an 8,192-token chunk (16 heads, d = 128, 128-token pages).
+EXTEND_CHUNK_LENS = (32768, 65536, 98304, 131072)
+EXTEND_CHUNK_QLENS = (8192, 8192, 8192, 8192)
+EXTEND_SEED = 1006
+# Multi-token decode workload: the latent decode shape (32 sequences at 128K
+# tokens, 64 query heads on one 576-wide latent head) with four new tokens
+# per sequence (the current token and three draft tokens).
+EXTEND_MTP_LEN = 131072
+EXTEND_MTP_Q = 4
+EXTEND_MTP_SEED = 1007
+
+
+@dataclass
+class ExtendInputs:
+    q: torch.Tensor            # [total_q, Hq, d_qk] packed rows of the new tokens
+    k_cache: torch.Tensor      # [pages, page_size, Hkv, d_qk]
+    v_cache: torch.Tensor      # [pages, page_size, Hkv, d_v] (a view of k_cache when latent)
+    page_table: torch.Tensor   # [B, max_pages] int32
+    ctx_lens: torch.Tensor     # [B] int32, new tokens included
+    cu_q: torch.Tensor         # [B + 1] int32 prefix sums of the chunk lengths
+    table_np: np.ndarray
+    lens: tuple
+    qlens: tuple
+
+
+def extend_inputs(lens, qlens, Hq: int, Hkv: int, d_qk: int, d_v: int, dtype: torch.dtype, device,
+                  seed: int, *, page_size: int = PAGE_SIZE, latent: bool = False,
+                  spare_pages: int = 0) -> ExtendInputs:
+    """A shuffled paged cache holding each sequence's lens[b] tokens and the
+    queries of its last qlens[b] tokens, packed by sequence."""
+    lens, qlens = tuple(int(x) for x in lens), tuple(int(x) for x in qlens)
+    table, num_pages = page_table_for(lens, page_size, seed, spare_pages)
+    gen = generator(device, seed)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = randn((int(cu[-1]), Hq, d_qk), dtype, device, gen)
+    k_cache = randn((num_pages, page_size, Hkv, d_qk), dtype, device, gen)
+    v_cache = k_cache[..., :d_v] if latent else randn((num_pages, page_size, Hkv, d_v), dtype, device, gen)
+    return ExtendInputs(q, k_cache, v_cache, torch.from_numpy(table).to(device),
+                        torch.tensor(lens, dtype=torch.int32, device=device),
+                        torch.from_numpy(cu).to(device), table, lens, qlens)
+
+
 def prefill_grad(cfg: PrefillConfig, device, seed: int | None = None):
     """Upstream gradient dout [B, N, Hq, d_v] for the backward of a prefill workload."""
     gen = generator(device, cfg.seed + 50 if seed is None else seed)

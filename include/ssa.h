@@ -237,6 +237,56 @@ size_t ssa_decode_workspace_size(ssa_dtype dtype, int32_t batch, int32_t heads_q
                                  int32_t page_size, int32_t max_pages, ssa_pattern pattern,
                                  int full);
 
+/*
+ * ssa_extend - several new query tokens per sequence against the paged KV
+ * cache, each attending to its own SSA window: a prefill chunk appended to a
+ * cached prefix (chunked prefill), or the few tokens of a multi-token decode
+ * step (speculative or multi-token-prediction drafts; the SSA paragraph of
+ * the digest's section 01 part (1) defines the window per query position,
+ * and section 02 measures the decode and prefill phases it serves).
+ *
+ * Sequence b has q_len_b = cu_q[b+1] - cu_q[b] new tokens at positions
+ * ctx_lens[b] - q_len_b .. ctx_lens[b] - 1; their keys and values are
+ * already in the cache (append, then attend). Row r of the chunk (packed row
+ * cu_q[b] + r) attends exactly as a decode step at context length
+ * ctx_lens[b] - q_len_b + r + 1 would, so causality inside the chunk holds.
+ *
+ *   q          [total_q, heads_q, d_qk] contiguous, rows packed by sequence.
+ *   k_cache, v_cache, k_strides, v_strides, page_table, max_pages,
+ *   page_size  as in ssa_decode.
+ *   ctx_lens   [batch] int32 context lengths, the new tokens included.
+ *   cu_q       [batch + 1] int32 prefix sums of the chunk lengths: cu_q[0] = 0,
+ *              non-decreasing, cu_q[batch] = total_q, and q_len_b <= ctx_lens[b]
+ *              (device data: trusted, not checked on the host).
+ *   max_q_len  an upper bound of every q_len_b (host value, >= 1 when
+ *              total_q > 0); rows beyond it are not computed.
+ *   o          [total_q, heads_q, d_v] contiguous, written; lse [total_q,
+ *              heads_q] fp32 or NULL.
+ *   workspace  device scratch of at least ssa_extend_workspace_size(...)
+ *              bytes (0 is possible); calls sharing it must not overlap.
+ * Kernels: bf16 with (d_qk, d_v) in {(64,64), (128,128), (192,128)} takes a
+ * paged tile kernel (128 rows of one sequence per work-group) when some chunk
+ * is longer than 8 rows or no decode kernel fits; otherwise, and for every
+ * shape ssa_decode compiles (fp32, the latent shape), each row runs as a
+ * decode step. batch == 0 or total_q == 0 is a no-op.
+ */
+ssa_status ssa_extend(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
+                      const int64_t k_strides[3], const int64_t v_strides[3],
+                      const int32_t *page_table, int32_t max_pages, const int32_t *ctx_lens,
+                      const int32_t *cu_q, int32_t batch, int32_t total_q, int32_t max_q_len,
+                      int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                      int32_t page_size, void *o, float *lse, void *workspace,
+                      size_t workspace_bytes, ssa_pattern pattern, float scale,
+                      hipStream_t stream);
+
+/*
+ * Workspace bytes for ssa_extend with the same shape arguments; 0 when the
+ * call needs none (the tile kernel), is empty, or would be rejected.
+ */
+size_t ssa_extend_workspace_size(ssa_dtype dtype, int32_t batch, int32_t total_q, int32_t max_q_len,
+                                 int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
+                                 int32_t page_size, int32_t max_pages, ssa_pattern pattern);
+
 /* Static, human-readable name of a status code. */
 const char *ssa_status_string(ssa_status status);
 

@@ -178,6 +178,34 @@ def decode_paged(q, k_cache, v_cache, page_table, ctx_lens, *, block=128, sink=1
     return o, lse
 
 
+def extend(q, k_cache, v_cache, page_table, ctx_lens, cu_q, *, block=128, sink=1, local=7, scale):
+    """New tokens of each sequence against the paged cache (chunked prefill,
+    multi-token decode). Sequence b's rows cu_q[b] .. cu_q[b+1]-1 sit at the
+    last q_len_b positions of its ctx_lens[b] tokens; a row at position p
+    attends exactly as one decode step at context length p + 1 (the SSA
+    paragraph defines the window per query position; decode puts the query at
+    the last position of its context). Each row is handed to ``decode_paged``
+    with its own context length and its sequence's page-table row.
+
+    q [total_q, Hq, d_qk]. Returns ``(o, lse)``: [total_q, Hq, d_v] and
+    [total_q, Hq] in float64.
+    """
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int64)
+    page_table = np.asarray(page_table, dtype=np.int32)
+    B = ctx_lens.shape[0]
+    if cu_q.shape != (B + 1,) or cu_q[0] != 0 or np.any(np.diff(cu_q) < 0) or cu_q[-1] != q.shape[0]:
+        raise ValueError("cu_q must be non-decreasing prefix sums from 0 to total_q")
+    q_len = np.diff(cu_q)
+    if np.any(q_len > ctx_lens):
+        raise ValueError("a chunk is longer than its context")
+    seq = np.repeat(np.arange(B), q_len)
+    r = np.arange(q.shape[0]) - cu_q[seq]
+    row_ctx = (ctx_lens[seq] - q_len[seq] + r + 1).astype(np.int32)
+    return decode_paged(q, k_cache, v_cache, page_table[seq], row_ctx, block=block, sink=sink,
+                        local=local, scale=scale)
+
+
 def backward(q, k, v, dout, *, block=128, sink=1, local=7, scale, full=False, rows=None):
     """Gradients of the prefill operator for the upstream gradient ``dout``.
 

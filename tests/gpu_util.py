@@ -79,8 +79,26 @@ def compact_paged(k_cache, v_cache, table_np, lens, page_size, block, sink, loca
                   latent_dv=None):
     """Copy to the host only the pages the oracle will read; every other logical
     page points to a NaN page, so a wrong read by the oracle would show."""
-    B = len(lens)
     need = [attended_logical_pages(L, page_size, block, sink, local, full) for L in lens]
+    return compact_pages(k_cache, v_cache, table_np, need, latent_dv)
+
+
+def rows_logical_pages(L: int, positions, page_size: int, block: int, sink: int, local: int):
+    """Logical pages holding a key that some query at one of `positions`
+    (all < L) attends: the sink blocks and [lo(min position), max position]."""
+    if len(positions) == 0:
+        return np.zeros(0, dtype=np.int64)
+    pmin, pmax = int(min(positions)), int(max(positions))
+    j = np.arange(pmax + 1)
+    lo = max(0, (pmin // block - local + 1) * block)
+    keep = (j // block < sink) | (j >= lo)
+    return np.unique(j[keep] // page_size)
+
+
+def compact_pages(k_cache, v_cache, table_np, need, latent_dv=None):
+    """Host copy of the logical pages need[b] of each sequence b, renumbered;
+    every other page of the table points to a NaN page."""
+    B = len(need)
     phys = np.concatenate([table_np[b, need[b]] for b in range(B)] + [np.zeros(0, np.int64)])
     phys_t = torch.from_numpy(phys.astype(np.int64)).to(k_cache.device)
     kh = host(k_cache[phys_t]) if phys.size else None

@@ -193,3 +193,44 @@ def test_dual_validation():
     assert dual_call(dtype=0) == UNSUPPORTED                # fp32 has no dual kernel
     assert dual_call(dqk=96, dv=96) == UNSUPPORTED
     assert dual_call(N=0) == OK and dual_call(B=0) == OK   # no-op
+
+
+def extend_call(dtype=1, B=2, total_q=6, max_q=4, Hq=4, Hkv=4, dqk=128, dv=128, ps=128, max_pages=8,
+                pattern=(128, 1, 7), ws_bytes=1 << 30, ptr=FAKE, scale=0.1):
+    lib = ssa.load_library()
+    ks = strides(ps * Hkv * dqk, Hkv * dqk, dqk)
+    p = ctypes.c_void_p(ptr) if ptr is not None else None
+    return lib.ssa_extend(dtype, p, p, p, ks, ks, p, max_pages, p, p, B, total_q, max_q, Hq, Hkv, dqk,
+                          dv, ps, p, None, p, ws_bytes, ssa.Pattern(*pattern), scale, None)
+
+
+def test_extend_validation():
+    assert extend_call(dtype=5) == INVALID
+    assert extend_call(B=-1) == INVALID
+    assert extend_call(total_q=-1) == INVALID
+    assert extend_call(max_q=0) == INVALID                  # rows exist, so some chunk is >= 1
+    assert extend_call(Hq=4, Hkv=3) == INVALID
+    assert extend_call(pattern=(128, 1, 0)) == INVALID
+    assert extend_call(ps=0) == INVALID
+    assert extend_call(scale=0.0) == INVALID
+    assert extend_call(ptr=None) == INVALID
+    assert extend_call(ptr=FAKE + 4) == INVALID
+    assert extend_call(dqk=96, dv=96) == UNSUPPORTED
+    assert extend_call(ws_bytes=0) == WORKSPACE             # short chunks: decode kernels need scratch
+    assert extend_call(B=0, ptr=None) == OK and extend_call(total_q=0, max_q=0, ptr=None) == OK
+
+
+def test_extend_workspace_sizes():
+    lib = ssa.load_library()
+    pat = ssa.Pattern(128, 1, 7)
+    # short chunks on a decode shape: row map + decode partials
+    short = lib.ssa_extend_workspace_size(1, 2, 6, 4, 4, 4, 128, 128, 128, 8, pat)
+    dec = lib.ssa_decode_workspace_size(1, 6, 4, 4, 128, 128, 128, 8, pat, 0)
+    assert short == 256 + dec
+    # a long chunk takes the tile kernel: no workspace
+    assert lib.ssa_extend_workspace_size(1, 2, 600, 500, 4, 4, 128, 128, 128, 8, pat) == 0
+    # d_qk = 192 has no decode kernel: tiles even for short chunks
+    assert lib.ssa_extend_workspace_size(1, 2, 6, 4, 4, 4, 192, 128, 128, 8, pat) == 0
+    # fp32 has no tile kernel: decode kernels even for long chunks
+    assert lib.ssa_extend_workspace_size(0, 2, 600, 500, 4, 4, 128, 128, 128, 8, pat) > 0
+    assert lib.ssa_extend_workspace_size(1, 0, 6, 4, 4, 4, 128, 128, 128, 8, pat) == 0
