@@ -104,6 +104,21 @@ __device__ __forceinline__ void dma16_untracked(const void *src, uint32_t lds_wa
         : "memory");
 }
 
+// A 4-byte untracked global -> LDS transfer: lane i's dword lands at
+// lds_wave_base + 4 i. Same contract as dma16_untracked.
+__device__ __forceinline__ void dma4_untracked(const void *src, uint32_t lds_wave_base) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds_wave_base)
+        : "memory");
+}
+
 // max(x, x from lane ^ 16) and max(x, x from lane ^ 32) on the VALU (gfx950
 // permlane swaps), instead of an LDS round trip through ds_bpermute.
 __device__ __forceinline__ float max_xor16(float x) {

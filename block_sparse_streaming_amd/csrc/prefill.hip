@@ -180,7 +180,14 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         }
     }
     // Paged mode: lane l holds the page and slot of key row l of the next
-    // sub-tile to be issued (rows past the range end take its last row).
+    // sub-tile to be issued (rows past the range end take its last row). The
+    // page id comes by a direct transfer into a per-wave LDS slot when the
+    // LDS budget of two work-groups per CU leaves room (an explicit counter
+    // wait then covers exactly that transfer); otherwise by a register load,
+    // before whose use the compiler waits for every transfer in flight.
+    constexpr int kLdsBytes = 2 * kBN * (DQK + DV) * 2;
+    constexpr bool kIdsInLds = PAGED && 2 * (kLdsBytes + 4 * 64 * 4) <= 160 * 1024;
+    __shared__ int32_t id_slot[kIdsInLds ? 4 * 64 : 1];
     const int32_t *ptab = PAGED ? a.page_table + (int64_t)bb * a.max_pages : nullptr;
     int pg_next = 0, sl_next = 0;
     auto read_ids = [&](int t) __attribute__((always_inline)) {
@@ -188,16 +195,41 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         const int tok = st.j0 + imin(lane, st.re - st.j0 - 1);
         const int lp = tok / a.page_size;
         sl_next = tok - lp * a.page_size;
-        pg_next = ptab[lp];
+        if constexpr (kIdsInLds) dma4_untracked(ptab + lp, lds_addr(id_slot) + wave * 256);
+        else pg_next = ptab[lp];
     };
     auto issue_paged = [&](int t, uint16_t *kb, uint16_t *vb) __attribute__((always_inline)) {
         const SubTile st = sub_tile<false>(tr, t);
         const int rows_valid = st.re - st.j0;
-        const int pg = pg_next, sl = sl_next;
+        int pg;
+        if constexpr (kIdsInLds) {
+            // In flight: this stage's ids, then the previous stage's transfers.
+            wait_vmcnt<NDMA>();
+            asm volatile("" ::: "memory");
+            pg = id_slot[wave * 64 + lane];
+            wait_lgkmcnt0();  // read before the next transfer rewrites the slot
+            asm volatile("" ::: "memory");
+        } else {
+            pg = pg_next;
+        }
+        const int sl = sl_next;
         // Read the next stage's ids before this stage's transfers, so that the
         // transfers stay the youngest operations in flight. The last stage
         // re-reads its own ids, which keeps the count fixed.
         read_ids(imin(t + 1, tr.n_total - 1));
+        // A full sub-tile inside one page (pages of 64 tokens or more, blocks
+        // aligned to 64): one page base and the contiguous path's offsets.
+        const int sl0 = __builtin_amdgcn_readfirstlane(sl);
+        if (kKeepOffsets && rows_valid >= kBN && sl0 + kBN <= a.page_size) {
+            const int64_t pg0 = __builtin_amdgcn_readfirstlane(pg);
+            const char *kt = (const char *)(kbase + pg0 * a.ks[0] + (int64_t)sl0 * a.ks[1]);
+            const char *vt = (const char *)(vbase + pg0 * a.vs[0] + (int64_t)sl0 * a.vs[1]);
+#pragma unroll
+            for (int n = 0; n < NIK; ++n) dma16(kt + koff[n], kb + (wave * NIK + n) * 512);
+#pragma unroll
+            for (int n = 0; n < NIV; ++n) dma16(vt + voff[n], vb + (wave * NIV + n) * 512);
+            return;
+        }
         auto src = [&](int p, int C, int swz, int64_t s0, int64_t s1) __attribute__((always_inline)) {
             const int row = imin(p / C, rows_valid - 1);
             const int64_t page = __shfl(pg, row), slot = __shfl(sl, row);
@@ -441,7 +473,10 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     const int T = DUAL ? tr.n_all : tr.n_total;
     int t = 0;
     if (T > 0) {
-        if constexpr (PAGED) read_ids(0);
+        if constexpr (PAGED) {
+            read_ids(0);
+            wait_vmcnt<0>();
+        }
         issue(0, k_buf0, v_buf0);
     }
     for (; t + 2 < T; t += 2) {

@@ -265,10 +265,11 @@ size_t ssa_decode_workspace_size(ssa_dtype dtype, int32_t batch, int32_t heads_q
  *   workspace  device scratch of at least ssa_extend_workspace_size(...)
  *              bytes (0 is possible); calls sharing it must not overlap.
  * Kernels: bf16 with (d_qk, d_v) in {(64,64), (128,128), (192,128)} takes a
- * paged tile kernel (128 rows of one sequence per work-group) when some chunk
- * is longer than 8 rows or no decode kernel fits; otherwise, and for every
- * shape ssa_decode compiles (fp32, the latent shape), each row runs as a
- * decode step. batch == 0 or total_q == 0 is a no-op.
+ * paged tile kernel (128 rows of one sequence per work-group) when max_q_len
+ * > 1 or no decode kernel fits; otherwise, and for the other shapes
+ * ssa_decode compiles (fp32, d = 256, the latent shape), each row runs as a
+ * decode step, with at most 65,535 rows per call. The tile kernel needs slot
+ * strides below 2^24 elements. batch == 0 or total_q == 0 is a no-op.
  */
 ssa_status ssa_extend(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
                       const int64_t k_strides[3], const int64_t v_strides[3],

@@ -195,7 +195,7 @@ def test_dual_validation():
     assert dual_call(N=0) == OK and dual_call(B=0) == OK   # no-op
 
 
-def extend_call(dtype=1, B=2, total_q=6, max_q=4, Hq=4, Hkv=4, dqk=128, dv=128, ps=128, max_pages=8,
+def extend_call(dtype=1, B=2, total_q=2, max_q=1, Hq=4, Hkv=4, dqk=128, dv=128, ps=128, max_pages=8,
                 pattern=(128, 1, 7), ws_bytes=1 << 30, ptr=FAKE, scale=0.1):
     lib = ssa.load_library()
     ks = strides(ps * Hkv * dqk, Hkv * dqk, dqk)
@@ -216,21 +216,24 @@ def test_extend_validation():
     assert extend_call(ptr=None) == INVALID
     assert extend_call(ptr=FAKE + 4) == INVALID
     assert extend_call(dqk=96, dv=96) == UNSUPPORTED
-    assert extend_call(ws_bytes=0) == WORKSPACE             # short chunks: decode kernels need scratch
+    assert extend_call(ws_bytes=0) == WORKSPACE             # one-row chunks: decode kernels need scratch
     assert extend_call(B=0, ptr=None) == OK and extend_call(total_q=0, max_q=0, ptr=None) == OK
 
 
 def test_extend_workspace_sizes():
     lib = ssa.load_library()
     pat = ssa.Pattern(128, 1, 7)
-    # short chunks on a decode shape: row map + decode partials
-    short = lib.ssa_extend_workspace_size(1, 2, 6, 4, 4, 4, 128, 128, 128, 8, pat)
+    # one-row chunks on a decode shape: row map + decode partials
+    short = lib.ssa_extend_workspace_size(1, 6, 6, 1, 4, 4, 128, 128, 128, 8, pat)
     dec = lib.ssa_decode_workspace_size(1, 6, 4, 4, 128, 128, 128, 8, pat, 0)
     assert short == 256 + dec
-    # a long chunk takes the tile kernel: no workspace
+    # two or more rows take the tile kernel: no workspace
+    assert lib.ssa_extend_workspace_size(1, 2, 4, 2, 4, 4, 128, 128, 128, 8, pat) == 0
     assert lib.ssa_extend_workspace_size(1, 2, 600, 500, 4, 4, 128, 128, 128, 8, pat) == 0
-    # d_qk = 192 has no decode kernel: tiles even for short chunks
-    assert lib.ssa_extend_workspace_size(1, 2, 6, 4, 4, 4, 192, 128, 128, 8, pat) == 0
+    # d_qk = 192 has no decode kernel: tiles even for one-row chunks
+    assert lib.ssa_extend_workspace_size(1, 2, 2, 1, 4, 4, 192, 128, 128, 8, pat) == 0
+    # d = 256 has no tile kernel: decode kernels for any chunk
+    assert lib.ssa_extend_workspace_size(1, 2, 8, 4, 4, 4, 256, 256, 128, 8, pat) > 0
     # fp32 has no tile kernel: decode kernels even for long chunks
     assert lib.ssa_extend_workspace_size(0, 2, 600, 500, 4, 4, 128, 128, 128, 8, pat) > 0
     assert lib.ssa_extend_workspace_size(1, 0, 6, 4, 4, 4, 128, 128, 128, 8, pat) == 0

@@ -2,9 +2,10 @@
 cache: multi-token decode and chunked prefill) against the CPU oracle,
 through the C ABI.
 
-Both kernels are covered: chunks of at most 8 rows on shapes the decode
-kernels compile run as decode steps over query rows; longer chunks (and the
-bf16 d_qk = 192 shape) take the paged tile kernel. Every row of every case is
+Both kernels are covered: one-row chunks, and every chunk on shapes only
+the decode kernels compile (fp32, d = 256, the latent shape), run as decode
+steps over query rows; longer chunks on bf16 d = 64 / 128 / 192 take the
+paged tile kernel, short multi-token chunks included. Every row of every case is
 compared with the oracle, which evaluates each row as one decode step at its
 own context length. The oracle reads only the pages the rows attend (the rest
 are NaN), so a wrong page read by either side would show.
@@ -64,7 +65,8 @@ def _inp(lens, qlens, Hq, Hkv, dqk, dv, dtype=torch.bfloat16, seed=0, **kw):
     return inputs.extend_inputs(lens, qlens, Hq, Hkv, dqk, dv, dtype, DEV, seed, **kw)
 
 
-# Multi-token decode (chunks of 1-8 rows): the decode kernels over query rows.
+# Multi-token decode (chunks of 1-8 rows): decode kernels for fp32, d = 256 and
+# the latent shape, the tile kernel for bf16 d = 64 / 128.
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_multi_token_decode_mha(dtype):
     lens = (1, 4, 127, 128, 129, 1023, 1024, 1025, 5000, 3)
@@ -97,7 +99,20 @@ def test_multi_token_decode_patterns(pattern):
          128 ** -0.5, f"mtp {pattern}")
 
 
-# Chunked prefill (chunks longer than 8 rows): the paged tile kernel.
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
+def test_one_row_chunks_equal_decode_bitwise(Hq, Hkv):
+    """bf16 one-row chunks take the decode kernels over query rows: each row
+    equals ssa_decode of the same sequence bit for bit, and the oracle."""
+    lens = (1, 127, 128, 129, 1025, 5000, 40000)
+    inp = _inp(lens, (1,) * len(lens), Hq, Hkv, 128, 128, seed=735 + Hq, spare_pages=2)
+    o, lse = _run(inp, PAT, 128 ** -0.5, f"one-row chunks g{Hq // Hkv}")
+    od, ld = ssa.decode(inp.q, inp.k_cache, inp.v_cache, inp.page_table, inp.ctx_lens, **PAT,
+                        scale=128 ** -0.5, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), od.view(torch.int16)) and torch.equal(lse, ld)
+
+
+# Chunked prefill (chunks longer than one row): the paged tile kernel.
 @pytest.mark.parametrize("dqk,dv,Hq,Hkv", [(128, 128, 2, 2), (128, 128, 4, 1), (64, 64, 4, 2),
                                            (192, 128, 2, 1)])
 def test_chunked_prefill_shapes(dqk, dv, Hq, Hkv):
@@ -157,12 +172,13 @@ def test_chunked_prefill_full_size_sampled():
 
 
 def test_rejects_small_workspace():
-    inp = _inp((500, 600), (3, 2), 4, 4, 128, 128, seed=790)
-    need = ssa.extend_workspace_size(torch.bfloat16, 2, 5, 3, 4, 4, 128, 128, inputs.PAGE_SIZE,
+    """One-row chunks run on the decode kernels, which need the workspace."""
+    inp = _inp((500, 600), (1, 1), 4, 4, 128, 128, seed=790)
+    need = ssa.extend_workspace_size(torch.bfloat16, 2, 2, 1, 4, 4, 128, 128, inputs.PAGE_SIZE,
                                      inp.page_table.shape[1])
     assert need > 0
     ws = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
     with pytest.raises(ssa.SSAError) as e:
-        ssa.extend(inp.q, inp.k_cache, inp.v_cache, inp.page_table, inp.ctx_lens, inp.cu_q, 3,
+        ssa.extend(inp.q, inp.k_cache, inp.v_cache, inp.page_table, inp.ctx_lens, inp.cu_q, 1,
                    workspace=ws)
     assert e.value.status == 3
