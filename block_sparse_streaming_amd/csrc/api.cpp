@@ -556,7 +556,7 @@ ssa_status ssa_extend(ssa_dtype dtype, const void *q, const void *k_cache, const
          v_strides[2] != k_strides[2]))
         return SSA_ERR_UNSUPPORTED;
     if ((int64_t)total_q * heads_q > kInt32Max || (int64_t)heads_kv * dp.head_chunks > 65535 ||
-        total_q > 65535 || heads_q > 65535 ||
+        total_q > 65535 || batch > 65535 || heads_q > 65535 ||
         (int64_t)dp.max_splits * heads_kv * dp.head_chunks * total_q > kInt32Max)
         return SSA_ERR_UNSUPPORTED;
     if (!workspace || !aligned16(workspace) || workspace_bytes < plan.total) return SSA_ERR_WORKSPACE;
@@ -592,7 +592,9 @@ ssa_status ssa_extend(ssa_dtype dtype, const void *q, const void *k_cache, const
     a.plan = dp;
     a.row_seq = row_seq;
     a.row_ctx = row_ctx;
-    if (ssa::launch_extend_rows(cu_q, ctx_lens, batch, total_q, row_seq, row_ctx, stream) != hipSuccess)
+    a.n_seqs = batch;
+    if (ssa::launch_extend_rows(cu_q, ctx_lens, batch, max_q_len, total_q, row_seq, row_ctx, stream) !=
+        hipSuccess)
         return SSA_ERR_HIP;
     return ssa::launch_decode(dtype == SSA_BF16, d_qk, d_v, a, stream) == hipSuccess ? SSA_OK : SSA_ERR_HIP;
 }

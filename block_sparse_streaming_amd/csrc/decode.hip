@@ -44,11 +44,17 @@ struct Sel {
 };
 
 // Context length (query position + 1) and page-table row of query row r.
+// Row-map entries are clamped to the table (a row the map left unwritten,
+// of a chunk longer than max_q_len, reads only valid pages).
 __device__ __forceinline__ int64_t row_context(const DecodeArgs &a, int r) {
-    return a.row_ctx ? (int64_t)a.row_ctx[r] : (int64_t)a.ctx_lens[r];
+    if (!a.row_ctx) return a.ctx_lens[r];
+    const int64_t L = a.row_ctx[r], cap = (int64_t)a.max_pages * a.page_size;
+    return L < cap ? L : cap;
 }
 __device__ __forceinline__ int64_t row_sequence(const DecodeArgs &a, int r) {
-    return a.row_seq ? (int64_t)a.row_seq[r] : (int64_t)r;
+    if (!a.row_seq) return r;
+    const int s = a.row_seq[r];
+    return s < 0 ? 0 : (s >= a.n_seqs ? a.n_seqs - 1 : s);
 }
 
 __device__ __forceinline__ Sel select_tokens(int64_t L, const DecodeArgs &a) {
@@ -643,23 +649,18 @@ hipError_t launch_valu_d(int d, const DecodeArgs &a, hipStream_t stream) {
 }
 
 
-// One thread per packed query row: its sequence (the last b with
-// cu_q[b] <= r, by binary search) and its context length. The length is
-// clamped to the sequence's, so malformed prefix sums stay within the cache.
+// Row map of packed query rows. Work-group (x, b) writes rows
+// cu_q[b] + 256 x + tid of sequence b: one round of (uniform) loads, no search.
+// Writes stay inside [0, total_q) whatever the prefix sums hold, and the
+// length is clamped to the sequence's.
 __global__ __launch_bounds__(256) void extend_rows(const int32_t *cu_q, const int32_t *ctx_lens,
-                                                   int32_t batch, int32_t total_q, int32_t *row_seq,
-                                                   int32_t *row_ctx) {
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    if (r >= total_q) return;
-    int lo = 0, hi = batch - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu_q[mid] <= r) lo = mid;
-        else hi = mid - 1;
-    }
-    const int ctx = ctx_lens[lo];
-    const int v = ctx - (cu_q[lo + 1] - 1 - r);
-    row_seq[r] = lo;
+                                                   int32_t total_q, int32_t *row_seq, int32_t *row_ctx) {
+    const int b = blockIdx.y;
+    const int r0 = cu_q[b], r1 = cu_q[b + 1], ctx = ctx_lens[b];
+    const int r = r0 + blockIdx.x * 256 + threadIdx.x;
+    if (r >= r1 || r < 0 || r >= total_q) return;
+    const int v = ctx - (r1 - 1 - r);
+    row_seq[r] = b;
     row_ctx[r] = v < ctx ? v : ctx;
 }
 
@@ -703,10 +704,11 @@ hipError_t launch_decode(bool bf16, int d_qk, int d_v, const DecodeArgs &a, hipS
 }
 
 hipError_t launch_extend_rows(const int32_t *cu_q, const int32_t *ctx_lens, int32_t batch,
-                              int32_t total_q, int32_t *row_seq, int32_t *row_ctx, hipStream_t stream) {
-    void *args[] = {(void *)&cu_q, (void *)&ctx_lens, (void *)&batch, (void *)&total_q, (void *)&row_seq,
-                    (void *)&row_ctx};
-    return hipLaunchKernel((const void *)extend_rows, dim3((total_q + 255) / 256), dim3(256), args, 0, stream);
+                              int32_t max_q_len, int32_t total_q, int32_t *row_seq, int32_t *row_ctx,
+                              hipStream_t stream) {
+    void *args[] = {(void *)&cu_q, (void *)&ctx_lens, (void *)&total_q, (void *)&row_seq, (void *)&row_ctx};
+    return hipLaunchKernel((const void *)extend_rows, dim3((max_q_len + 255) / 256, batch), dim3(256), args,
+                           0, stream);
 }
 
 }  // namespace ssa

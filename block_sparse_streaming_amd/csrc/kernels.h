@@ -105,6 +105,7 @@ struct DecodeArgs {
     // + 1). Null for one row per sequence (row r = sequence r, ctx_lens[r]).
     const int32_t *row_seq;
     const int32_t *row_ctx;
+    int32_t n_seqs;                 // sequences (page-table rows) when row_seq is set
 };
 
 bool decode_valu_supported(bool bf16, int d_qk, int d_v, int group);
@@ -113,7 +114,9 @@ hipError_t launch_decode(bool bf16, int d_qk, int d_v, const DecodeArgs &a, hipS
 
 // Row map of packed query rows: row r of sequence b (cu_q[b] <= r < cu_q[b+1])
 // gets row_seq[r] = b and row_ctx[r] = ctx_lens[b] - (cu_q[b+1] - 1 - r).
+// Rows past cu_q[b] + max_q_len are not written; no write leaves [0, total_q).
 hipError_t launch_extend_rows(const int32_t *cu_q, const int32_t *ctx_lens, int32_t batch,
-                              int32_t total_q, int32_t *row_seq, int32_t *row_ctx, hipStream_t stream);
+                              int32_t max_q_len, int32_t total_q, int32_t *row_seq, int32_t *row_ctx,
+                              hipStream_t stream);
 
 }  // namespace ssa
