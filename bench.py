@@ -10,14 +10,15 @@ workload and SSA decode on the ragged 4K-1M workload (HBM GB/s of algorithmic
 bytes), the prefill backward at 32K and 256K tokens (TFLOP/s), the dual
 forward (SSA, full causal attention and their alpha-mix in one pass) at 32K
 (TFLOP/s of full causal attention), chunked prefill and multi-token decode
-against the paged cache (TFLOP/s; GB/s), each against its roofline, and the
-CPU oracle timed on the prefill.
+against the paged cache (TFLOP/s; GB/s), hybrid decode over the window and
+a list of 1,024 tokens (GB/s), each against its roofline, and the CPU oracle
+timed on the prefill.
 
 Inputs are synthetic (seeded N(0,1)) and resident in HBM before timing.
 Timing uses HIP events recorded on the stream the kernels are launched on
 (torch's current stream, which the binding passes to the library).
 
---profile {prefill,decode,backward,dual,extend,copy} runs one short workload and prints nothing
+--profile {prefill,decode,backward,dual,extend,hybrid,copy} runs one short workload and prints nothing
 else, for rocprofv3 counter collection (copy: a plain 1 GiB device copy whose
 counter readings calibrate FETCH_SIZE / WRITE_SIZE).
 """
@@ -379,6 +380,97 @@ def bench_extend_mtp(iters: int):
 
 
 # ---------------------------------------------------------------------------
+# Hybrid decode: SSA window plus listed tokens
+# ---------------------------------------------------------------------------
+def hybrid_setup(n_inst: int):
+    """The hybrid decode workload: the latent decode shape (32 sequences at
+    128K, 64 heads) with 16 sink tokens, a 1,024-token window and 1,024 listed
+    tokens; n_inst page-table / query / list instances over one cache."""
+    import torch
+    from block_sparse_streaming_amd import inputs
+    B = 32
+    lens = (inputs.EXTEND_MTP_LEN,) * B
+    base = inputs.extend_inputs(lens, (1,) * B, 64, 1, 576, 512, torch.bfloat16, "cuda:0",
+                                inputs.HYBRID_SEED, latent=True)
+    insts = []
+    for r in range(n_inst):
+        table, _ = inputs.page_table_for(lens, inputs.PAGE_SIZE, seed=inputs.HYBRID_SEED + 100 + r)
+        g = inputs.generator("cuda:0", inputs.HYBRID_SEED + 200 + r)
+        qr = inputs.randn(tuple(base.q.shape), torch.bfloat16, "cuda:0", g)
+        lst = inputs.token_lists(lens, inputs.HYBRID_K, inputs.HYBRID_SEED + 300 + r)
+        insts.append((qr, torch.from_numpy(table).to("cuda:0"), torch.from_numpy(lst).to("cuda:0"), lst))
+    return base, insts
+
+
+def hybrid_bytes(lens, lists, block: int, sink: int, local: int, page_size: int, Hq: int) -> int:
+    """Algorithmic bytes of one hybrid call: the latent rows of the window and
+    of the listed tokens outside it (each once), q, o, the page ids of the
+    window's pages and of the listed rows, the lists and the lengths."""
+    rows = 0
+    pids = 0
+    for L, lst in zip(lens, lists):
+        j = np.arange(L)
+        win = (j // block < sink) | (j // block > (L - 1) // block - local)
+        extra = np.setdiff1d(lst[(lst >= 0) & (lst < L)], j[win])
+        rows += int(win.sum()) + extra.size
+        pids += np.unique(j[win] // page_size).size + extra.size
+    B = len(lens)
+    return (rows * 576 * 2 + B * Hq * (576 + 512) * 2 + pids * 4 + sum(len(x) for x in lists) * 4 +
+            B * 4)
+
+
+def bench_hybrid(iters: int):
+    """hybrid_decode on the hybrid workload, rotating over 8 instances and
+    replayed from a HIP graph, as the latent decode measurement does."""
+    import torch
+    import block_sparse_streaming_amd as ssa
+    from block_sparse_streaming_amd import inputs
+    n_inst = 8
+    base, insts = hybrid_setup(n_inst)
+    B, Hq = len(base.lens), 64
+    pat = inputs.HYBRID_PATTERN
+    max_pages = base.page_table.shape[1]
+    ws = torch.empty(ssa.hybrid_decode_workspace_size(torch.bfloat16, B, Hq, 1, 576, 512, inputs.PAGE_SIZE,
+                                                      max_pages, inputs.HYBRID_K, **pat),
+                     dtype=torch.uint8, device="cuda:0")
+    outs = [torch.empty((B, Hq, 512), dtype=torch.bfloat16, device="cuda:0") for _ in range(n_inst)]
+
+    def call(r):
+        qr, tr, lt, _ = insts[r]
+        ssa.hybrid_decode(qr, base.k_cache, base.v_cache, tr, base.ctx_lens, lt, **pat, scale=576 ** -0.5,
+                          out=outs[r], workspace=ws)
+
+    for r in range(n_inst):
+        call(r)
+    torch.cuda.synchronize()
+    reps = 4
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for _ in range(reps):
+                for r in range(n_inst):
+                    call(r)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ms = time_events(graph.replay, max(1, iters // (reps * n_inst))) / (reps * n_inst)
+    nbytes = int(np.mean([hybrid_bytes(base.lens, inst[3], **pat, page_size=inputs.PAGE_SIZE, Hq=Hq)
+                          for inst in insts]))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    splits = 17  # 1,040 window tokens and 1,024 listed ones in splits of 128
+    name = "hybrid_decode_bf16_latent_b32_h64_d576_L131072_sink16_win1024_top1024"
+    res = {"workload": name, "us": ms * 1e3, "bytes": nbytes, "GB/s": gbs,
+           "roofline": decode_roofline(gbs, [f"decode_split_latent grid={splits * B * 256}",
+                                             f"decode_merge<true, 512> grid={B * Hq * 64}"]),
+           "timing": f"HIP graph of {reps * n_inst} calls rotating over {n_inst} instances"}
+    del graph, insts, outs, base, ws
+    free_gpu()
+    return name, res
+
+
+# ---------------------------------------------------------------------------
 # Backward of prefill
 # ---------------------------------------------------------------------------
 def backward_flops(cfg) -> int:
@@ -636,6 +728,8 @@ def profile_run(what: str):
         _, step = dual_setup(2)
         for _ in range(3):
             step()
+    elif what == "hybrid":
+        bench_hybrid(32)
     elif what == "extend":
         _, step = extend_chunk_setup()
         for _ in range(3):
@@ -655,7 +749,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--profile", choices=["prefill", "decode", "backward", "dual", "extend", "copy"], default=None)
+    ap.add_argument("--profile", choices=["prefill", "decode", "backward", "dual", "extend", "hybrid", "copy"], default=None)
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the 32K prefill (and the CPU oracle)")
     args = ap.parse_args()
@@ -709,6 +803,9 @@ def main():
         name, r = bench_extend_mtp(256)
         workloads[name] = r
         note(f"extend {name}: {r['us']:.2f} us/call ({r['GB/s']:.0f} GB/s)")
+        name, r = bench_hybrid(256)
+        workloads[name] = r
+        note(f"hybrid {name}: {r['us']:.2f} us/call ({r['GB/s']:.0f} GB/s)")
     cpu = cpu_baseline()
     note(f"cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
     from block_sparse_streaming_amd import inputs

@@ -22,7 +22,8 @@ SSA_BF16 = 1
 # Exported symbols, in the order include/ssa.h declares them.
 EXPORTS = ("ssa_prefill", "ssa_prefill_dual", "ssa_prefill_backward", "ssa_prefill_backward_workspace_size",
            "ssa_decode", "full_attn_decode", "ssa_decode_workspace_size", "ssa_extend",
-           "ssa_extend_workspace_size", "ssa_status_string")
+           "ssa_extend_workspace_size", "hybrid_decode", "hybrid_decode_workspace_size",
+           "ssa_status_string")
 
 
 class SSAError(RuntimeError):
@@ -81,6 +82,12 @@ def load_library() -> ctypes.CDLL:
     lib.ssa_extend_workspace_size.restype = sz
     lib.ssa_extend_workspace_size.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, i32,
                                               i32, Pattern]
+    lib.hybrid_decode.restype = ctypes.c_int
+    lib.hybrid_decode.argtypes = [ctypes.c_int, p, p, p, i64p, i64p, p, i32, p, p, i32, i32, i32, i32,
+                                  i32, i32, i32, p, p, p, sz, Pattern, f32, p]
+    lib.hybrid_decode_workspace_size.restype = sz
+    lib.hybrid_decode_workspace_size.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                 Pattern]
     lib.ssa_status_string.restype = ctypes.c_char_p
     lib.ssa_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -372,4 +379,62 @@ def extend(q, k_cache, v_cache, page_table, ctx_lens, cu_q, max_q_len: int, *, b
                           B, total_q, int(max_q_len), Hq, Hkv, d_qk, d_v, page_size, _ptr(out),
                           _ptr(lse), _ptr(workspace), ws_bytes, Pattern(block, sink, local),
                           float(scale), _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def hybrid_decode_workspace_size(dtype: torch.dtype, batch: int, heads_q: int, heads_kv: int,
+                                 d_qk: int, d_v: int, page_size: int, max_pages: int, topk_k: int, *,
+                                 block: int = 1, sink: int = 16, local: int = 1024) -> int:
+    """Bytes of workspace hybrid_decode needs."""
+    code = SSA_BF16 if dtype == torch.bfloat16 else SSA_F32
+    return int(load_library().hybrid_decode_workspace_size(code, batch, heads_q, heads_kv, d_qk, d_v,
+                                                           page_size, max_pages, topk_k,
+                                                           Pattern(block, sink, local)))
+
+
+def hybrid_decode(q, k_cache, v_cache, page_table, ctx_lens, topk, *, block: int = 1, sink: int = 16,
+                  local: int = 1024, scale: float | None = None, out=None, workspace=None,
+                  return_lse: bool = False):
+    """hybrid_decode: ``decode`` over the SSA window (by default 16 sink
+    tokens and a 1,024-token window) plus the listed tokens topk [B, K] int32
+    (entries inside the window, past the context or negative are skipped)."""
+    lib = load_library()
+    _on_gpu(q, k_cache, v_cache, page_table, ctx_lens, topk)
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    for t in (page_table, ctx_lens, topk):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError("page_table, ctx_lens and topk must be contiguous int32")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    B, Hq, d_qk = q.shape
+    _, page_size, Hkv, d_qk2 = k_cache.shape
+    d_v = v_cache.shape[3]
+    if d_qk2 != d_qk or v_cache.shape[:3] != k_cache.shape[:3]:
+        raise ValueError("cache shape mismatch")
+    if page_table.dim() != 2 or page_table.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("page_table must be [B, max_pages] and ctx_lens [B]")
+    if topk.dim() != 2 or topk.shape[0] != B:
+        raise ValueError("topk must be [B, K]")
+    K = topk.shape[1]
+    max_pages = page_table.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, d_v), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, Hq, d_v) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Hq, d_v] tensor of q's dtype")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    need = hybrid_decode_workspace_size(q.dtype, B, Hq, Hkv, d_qk, d_v, page_size, max_pages, K,
+                                        block=block, sink=sink, local=local)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _on_gpu(workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.hybrid_decode(dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _strides3(k_cache),
+                             _strides3(v_cache), _ptr(page_table), max_pages, _ptr(ctx_lens),
+                             _ptr(topk), K, B, Hq, Hkv, d_qk, d_v, page_size, _ptr(out), _ptr(lse),
+                             _ptr(workspace), ws_bytes, Pattern(block, sink, local), float(scale),
+                             _stream(q.device)))
     return (out, lse) if return_lse else out

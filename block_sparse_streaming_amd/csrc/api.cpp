@@ -83,6 +83,16 @@ bool make_plan(ssa_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv
     return true;
 }
 
+// Hybrid decode: the listed tokens take splits of the same size after the
+// window's. Only the latent kernel reads a token list.
+bool add_list_splits(DecodePlan *plan, int32_t topk_k) {
+    if (plan->kind != ssa::kDecodeLatent) return false;
+    const int64_t n = plan->max_splits + ((int64_t)topk_k + plan->split_tokens - 1) / plan->split_tokens;
+    if (n > 65535) return false;
+    plan->max_splits = (int)n;
+    return true;
+}
+
 struct WorkspaceLayout {
     size_t o_bytes, lse_offset, total;
 };
@@ -102,8 +112,9 @@ ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, co
                          int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
                          int32_t page_size, void *o, float *lse, void *workspace,
                          size_t workspace_bytes, ssa_pattern pattern, float scale, bool full,
-                         hipStream_t stream) {
+                         hipStream_t stream, const int32_t *topk = nullptr, int32_t topk_k = 0) {
     if (!dtype_ok(dtype)) return SSA_ERR_INVALID_ARG;
+    if (topk_k < 0 || (topk_k > 0 && !topk && batch > 0)) return SSA_ERR_INVALID_ARG;
     if (batch < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv || d_qk < 1 || d_v < 1 ||
         page_size < 1 || max_pages < 1)
         return SSA_ERR_INVALID_ARG;
@@ -120,6 +131,7 @@ ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, co
     DecodePlan plan;
     if (!make_plan(dtype, batch, heads_q, heads_kv, d_qk, d_v, page_size, max_pages, pattern, full, &plan))
         return SSA_ERR_UNSUPPORTED;
+    if (topk_k > 0 && !add_list_splits(&plan, topk_k)) return SSA_ERR_UNSUPPORTED;
     if (plan.kind == ssa::kDecodeLatent) {
         // The latent kernel reads the value as the first d_v entries of the key row.
         if (v_cache != k_cache || v_strides[0] != k_strides[0] || v_strides[1] != k_strides[1] ||
@@ -159,6 +171,8 @@ ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, co
     a.ws_o = static_cast<float *>(workspace);
     a.ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + wl.lse_offset);
     a.plan = plan;
+    a.topk = topk_k > 0 ? topk : nullptr;
+    a.topk_k = topk_k;
     return ssa::launch_decode(dtype == SSA_BF16, d_qk, d_v, a, stream) == hipSuccess ? SSA_OK : SSA_ERR_HIP;
 }
 
@@ -611,6 +625,33 @@ size_t ssa_extend_workspace_size(ssa_dtype dtype, int32_t batch, int32_t total_q
                      pattern, &plan))
         return 0;
     return plan.total;
+}
+
+ssa_status hybrid_decode(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
+                         const int64_t k_strides[3], const int64_t v_strides[3],
+                         const int32_t *page_table, int32_t max_pages, const int32_t *ctx_lens,
+                         const int32_t *topk, int32_t topk_k, int32_t batch, int32_t heads_q,
+                         int32_t heads_kv, int32_t d_qk, int32_t d_v, int32_t page_size, void *o,
+                         float *lse, void *workspace, size_t workspace_bytes, ssa_pattern pattern,
+                         float scale, hipStream_t stream) {
+    if (topk_k < 1) return SSA_ERR_INVALID_ARG;
+    return decode_common(dtype, q, k_cache, v_cache, k_strides, v_strides, page_table, max_pages,
+                         ctx_lens, batch, heads_q, heads_kv, d_qk, d_v, page_size, o, lse, workspace,
+                         workspace_bytes, pattern, scale, false, stream, topk, topk_k);
+}
+
+size_t hybrid_decode_workspace_size(ssa_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                    int32_t d_qk, int32_t d_v, int32_t page_size, int32_t max_pages,
+                                    int32_t topk_k, ssa_pattern pattern) {
+    if (!dtype_ok(dtype) || batch < 1 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv ||
+        page_size < 1 || max_pages < 1 || d_qk < 1 || d_v < 1 || topk_k < 1 || !pattern_ok(pattern))
+        return 0;
+    DecodePlan plan;
+    if (!make_plan(dtype, batch, heads_q, heads_kv, d_qk, d_v, page_size, max_pages, pattern, false,
+                   &plan) ||
+        !add_list_splits(&plan, topk_k))
+        return 0;
+    return workspace_layout(batch, heads_q, d_v, plan).total;
 }
 
 const char *ssa_status_string(ssa_status status) {

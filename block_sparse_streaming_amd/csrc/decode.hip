@@ -57,6 +57,11 @@ __device__ __forceinline__ int64_t row_sequence(const DecodeArgs &a, int r) {
     return s < 0 ? 0 : (s >= a.n_seqs ? a.n_seqs - 1 : s);
 }
 
+// Splits of the listed tokens (hybrid decode); they follow the window's.
+__device__ __forceinline__ int list_splits(const DecodeArgs &a) {
+    return a.topk_k > 0 ? (a.topk_k + a.plan.split_tokens - 1) / a.plan.split_tokens : 0;
+}
+
 __device__ __forceinline__ Sel select_tokens(int64_t L, const DecodeArgs &a) {
     if (a.full) return Sel{L, L, L};
     const int64_t b = a.block, sb = (int64_t)a.sink * b;
@@ -294,6 +299,7 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     __shared__ __attribute__((aligned(1024))) uint16_t c_b3[kLatCh * kLatDqk];
     __shared__ int32_t pids[kLatMaxPages];
     __shared__ int64_t rowtab[4][kLatRowsPerWave];
+    __shared__ uint32_t vmask[kLatBufs];  // listed tokens: attended rows of each ring slot
 
     // Work-groups of one XCD (own L2) take whole sequences, so the splits of a
     // sequence share q in that L2.
@@ -309,10 +315,14 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     const int64_t L = row_context(a, bb);
     if (L <= 0) return;
     const Sel sel = select_tokens(L, a);
-    const int64_t p_begin = (int64_t)split * a.plan.split_tokens;
-    if (p_begin >= sel.total) return;
-    const int64_t p_end = p_begin + a.plan.split_tokens < sel.total ? p_begin + a.plan.split_tokens
-                                                                      : sel.total;
+    // Splits [0, n_win) cover the window's positions; the next list_splits(a)
+    // cover the listed tokens (hybrid decode), positions of the list.
+    const int n_win = (int)((sel.total + a.plan.split_tokens - 1) / a.plan.split_tokens);
+    const bool listed = split >= n_win;
+    const int64_t p_begin = (int64_t)(listed ? split - n_win : split) * a.plan.split_tokens;
+    const int64_t p_lim = listed ? (int64_t)a.topk_k : sel.total;
+    if (p_begin >= p_lim) return;
+    const int64_t p_end = p_begin + a.plan.split_tokens < p_lim ? p_begin + a.plan.split_tokens : p_lim;
     const int ntok = (int)(p_end - p_begin);
     const int nch = (ntok + kLatCh - 1) / kLatCh;
 
@@ -326,8 +336,10 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     const int64_t t2 = sel.r2_begin + (s2 - sel.r1_end);                  // first token of part 2
     const int64_t lp2 = t2 / P;
     const int n2 = p_end > s2 ? (int)((sel.r2_begin + (p_end - sel.r1_end) - 1) / P - lp2 + 1) : 0;
-    for (int t = tid; t < n1 + n2; t += kLatThreads)
-        pids[t] = a.page_table[row_sequence(a, bb) * a.max_pages + (t < n1 ? lp1 + t : lp2 + (t - n1))];
+    const int64_t seq = row_sequence(a, bb);
+    if (!listed)
+        for (int t = tid; t < n1 + n2; t += kLatThreads)
+            pids[t] = a.page_table[seq * a.max_pages + (t < n1 ? lp1 + t : lp2 + (t - n1))];
 
     const int heads_here = a.group - hc * 64 < 64 ? a.group - hc * 64 : 64;
     const bool active = wave * 16 < heads_here;
@@ -363,14 +375,33 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
         const int idx = pp < ur1 ? (int)(lp - ulp1) : n1 + (int)(lp - ulp2);
         return (int64_t)pids[idx] * a.ks[0] + (int64_t)(tok - lp * uP) * a.ks[1];
     };
+    // A listed token: its row, found through the list and the page table. A
+    // token inside the window, past the context or negative (padding) is
+    // skipped: its key is masked and token 0's row stands in for it.
+    const uint32_t uL = (uint32_t)L, ur2end = ur2 < uL ? ur2 : uL;
+    auto list_row_off = [&](uint32_t pp, bool &ok) __attribute__((always_inline)) -> int64_t {
+        pp = pp < up_end ? pp : up_end - 1;
+        const int t0 = a.topk[seq * a.topk_k + pp];
+        ok = t0 >= (int)ur1 && (uint32_t)t0 < ur2end;
+        const uint32_t tok = ok ? (uint32_t)t0 : 0u;
+        const uint32_t lp = tok / uP;
+        return (int64_t)a.page_table[seq * a.max_pages + lp] * a.ks[0] + (int64_t)(tok - lp * uP) * a.ks[1];
+    };
     // Transfers of chunk c: wave w moves rows 8w..8w+7. Lane slot p = 64n + lane
     // of its transfer n is row 8w + p / 72 at physical unit p % 72, which holds
     // logical unit (p % 72) ^ lat_swz(row). The wave's eight row offsets are
     // computed once by lanes 0..7 into rowtab (rows past the split's end
-    // repeat its last row).
+    // repeat its last row). For listed tokens, byte w of vmask[c % 4] says
+    // which of the wave's eight rows are attended.
     auto issue = [&](int c, uint16_t *buf) __attribute__((always_inline)) {
-        if (lane < kLatRowsPerWave) {
-            rowtab[wave][lane] = row_off((uint32_t)p_begin + (uint32_t)(c * kLatCh + wave * kLatRowsPerWave + lane));
+        const uint32_t pp = (uint32_t)p_begin + (uint32_t)(c * kLatCh + wave * kLatRowsPerWave + lane);
+        if (!listed) {
+            if (lane < kLatRowsPerWave) rowtab[wave][lane] = row_off(pp);
+        } else {
+            bool ok = false;
+            if (lane < kLatRowsPerWave) rowtab[wave][lane] = list_row_off(pp, ok);
+            const uint64_t bits = __builtin_amdgcn_ballot_w64(ok && lane < kLatRowsPerWave);
+            if (lane == 0) ((uint8_t *)&vmask[c % kLatBufs])[wave] = (uint8_t)bits;
         }
 #pragma unroll
         for (int n = 0; n < kLatDma; ++n) {
@@ -414,11 +445,14 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
                 s[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[tb], 0, 0, 0);
             }
         const int nvalid = ntok - c * kLatCh;
+        const uint32_t vm = listed ? vmask[c % kLatBufs] : 0xffffffffu;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (tb * 16 + 4 * kg + r >= nvalid) s[tb][r] = -INFINITY;
+            for (int r = 0; r < 4; ++r) {
+                const int t = tb * 16 + 4 * kg + r;
+                if (t >= nvalid || !((vm >> t) & 1u)) s[tb][r] = -INFINITY;
+            }
     };
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -445,11 +479,14 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
         }
         float p[8];
         float rs = 0.f;
+        // Before any attended key (possible only for listed tokens) m_run is
+        // -inf and every score of the chunk is masked: p = 0.
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[4 * tb + r] = fast_exp2(__builtin_fmaf(s[tb][r], a.scale_log2, -m_run));
+                p[4 * tb + r] = fast_exp2(__builtin_fmaf(s[tb][r], a.scale_log2, neg_m));
                 rs += p[4 * tb + r];
             }
         l_run += rs;
@@ -509,12 +546,14 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
     if (!active) return;
-    const float inv = 1.f / l_tot;
+    // A split with no attended key (all of its listed tokens skipped) writes
+    // o = 0 and lse = -inf, which the merge weights by zero.
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t slot = ((int64_t)bb * a.Hq + head) * a.plan.max_splits + split;
     float *wo = a.ws_o + slot * kLatDv + 4 * kg;
 #pragma unroll
     for (int d = 0; d < kLatDv / 16; ++d) *(f32x4 *)(wo + d * 16) = oacc[d] * inv;
-    if (kg == 0) a.ws_lse[slot] = m_run + log2f(l_tot);
+    if (kg == 0) a.ws_lse[slot] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -539,7 +578,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
     int ns = 0;
     if (L > 0) {
         const Sel sel = select_tokens(L, a);
-        ns = (int)((sel.total + a.plan.split_tokens - 1) / a.plan.split_tokens);
+        ns = (int)((sel.total + a.plan.split_tokens - 1) / a.plan.split_tokens) + list_splits(a);
     }
     if (ns == 0) {
 #pragma unroll

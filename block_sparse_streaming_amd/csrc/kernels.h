@@ -106,6 +106,11 @@ struct DecodeArgs {
     const int32_t *row_seq;
     const int32_t *row_ctx;
     int32_t n_seqs;                 // sequences (page-table rows) when row_seq is set
+    // Hybrid decode: besides the SSA window, each sequence attends the listed
+    // tokens topk[b * topk_k + i] that lie outside the window (others, and
+    // negative padding, are skipped). Their splits follow the window's.
+    const int32_t *topk;
+    int32_t topk_k;                 // 0: no list
 };
 
 bool decode_valu_supported(bool bf16, int d_qk, int d_v, int group);

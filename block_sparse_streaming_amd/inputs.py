@@ -199,6 +199,28 @@ def extend_inputs(lens, qlens, Hq: int, Hkv: int, d_qk: int, d_v: int, dtype: to
                         torch.from_numpy(cu).to(device), table, lens, qlens)
 
 
+def token_lists(lens, K: int, seed: int, *, pad_per_row: int = 0) -> np.ndarray:
+    """[B, K] int32 lists of distinct token positions drawn uniformly from
+    [0, L) of each sequence (an indexer's choice stands in for nothing more
+    than that), the last pad_per_row entries of a row and any entry beyond
+    L set to -1 (padding)."""
+    rng = np.random.default_rng(seed)
+    out = np.full((len(lens), K), -1, dtype=np.int32)
+    for b, L in enumerate(lens):
+        n = max(0, min(K - pad_per_row, int(L)))
+        if n:
+            out[b, :n] = rng.choice(int(L), n, replace=False)
+    return out
+
+
+# Hybrid decode workload: the latent decode shape (32 sequences at 128K, 64
+# query heads on one 576-wide latent head) with 16 sink tokens, a 1,024-token
+# window and 1,024 listed tokens per sequence.
+HYBRID_PATTERN = dict(block=1, sink=16, local=1024)
+HYBRID_K = 1024
+HYBRID_SEED = 1008
+
+
 def prefill_grad(cfg: PrefillConfig, device, seed: int | None = None):
     """Upstream gradient dout [B, N, Hq, d_v] for the backward of a prefill workload."""
     gen = generator(device, cfg.seed + 50 if seed is None else seed)

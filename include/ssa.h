@@ -288,6 +288,44 @@ size_t ssa_extend_workspace_size(ssa_dtype dtype, int32_t batch, int32_t total_q
                                  int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
                                  int32_t page_size, int32_t max_pages, ssa_pattern pattern);
 
+/*
+ * hybrid_decode - one-token decode over the SSA window of `pattern` plus a
+ * list of tokens chosen elsewhere, the two merged by log-sum-exp. It follows
+ * the streaming-aware indexing of "LongCat Sparse Attention" (agihunt.info,
+ * the streaming-aware indexing paragraph): of a 2,048-token budget, 16 sink
+ * tokens and a 1,024-token sliding window are fixed and contiguous, and
+ * 1,024 tokens come from an indexer; a hybrid kernel attends the fixed and
+ * the sparse part separately and merges them with online softmax. Here the
+ * fixed part is the SSA window (block 1, sink 16, local 1024 reproduces it
+ * token for token) and the list is an input: the indexer is not part of this
+ * library.
+ *
+ *   q, caches, strides, page_table, max_pages, ctx_lens, page_size, o, lse,
+ *   scale      as in ssa_decode.
+ *   topk       [batch, topk_k] int32 token positions, device memory. An entry
+ *              inside the window, at or past the context length, or negative
+ *              (padding) is skipped; entries must be distinct (a repeated
+ *              token would count twice). Trusted device data.
+ *   workspace  at least hybrid_decode_workspace_size(...) bytes.
+ * The window and the listed tokens are cut into splits of one size; one
+ * merge combines all of a row's splits. Compiled: the bf16 latent shape
+ * (d_qk = 576, d_v = 512, heads_q / heads_kv a multiple of 16); other shapes
+ * return SSA_ERR_UNSUPPORTED. topk_k must be >= 1.
+ */
+ssa_status hybrid_decode(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
+                         const int64_t k_strides[3], const int64_t v_strides[3],
+                         const int32_t *page_table, int32_t max_pages, const int32_t *ctx_lens,
+                         const int32_t *topk, int32_t topk_k, int32_t batch, int32_t heads_q,
+                         int32_t heads_kv, int32_t d_qk, int32_t d_v, int32_t page_size, void *o,
+                         float *lse, void *workspace, size_t workspace_bytes, ssa_pattern pattern,
+                         float scale, hipStream_t stream);
+
+/* Workspace bytes for hybrid_decode with the same shape arguments; 0 for
+ * arguments it would reject. */
+size_t hybrid_decode_workspace_size(ssa_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                    int32_t d_qk, int32_t d_v, int32_t page_size, int32_t max_pages,
+                                    int32_t topk_k, ssa_pattern pattern);
+
 /* Static, human-readable name of a status code. */
 const char *ssa_status_string(ssa_status status);
 

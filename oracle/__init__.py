@@ -206,6 +206,62 @@ def extend(q, k_cache, v_cache, page_table, ctx_lens, cu_q, *, block=128, sink=1
                         local=local, scale=scale)
 
 
+def _bf16_or_f32_to_f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def hybrid_decode(q, k_cache, v_cache, page_table, ctx_lens, topk, *, block=1, sink=16, local=1024,
+                  scale):
+    """One decode step over the SSA window plus listed tokens (the streaming-
+    aware indexing of "LongCat Sparse Attention": fixed sink and window
+    tokens, and tokens an indexer chose). For the query at position L - 1 the
+    attended set is the window of the block rule (j <= L - 1 with j // b < s
+    or j // b > (L - 1) // b - l) united with the listed positions that lie in
+    [0, L); negative entries are padding. One softmax over that set.
+
+    q [B, Hq, d_qk], caches [pages, page_size, Hkv, d], page_table [B,
+    max_pages], ctx_lens [B], topk [B, K]. Returns ``(o, lse)`` in float64;
+    L <= 0 gives zeros and -inf.
+    """
+    q64 = _bf16_or_f32_to_f64(q)
+    kc, vc = _bf16_or_f32_to_f64(k_cache), _bf16_or_f32_to_f64(v_cache)
+    page_table = np.asarray(page_table)
+    ctx_lens = np.asarray(ctx_lens)
+    topk = np.asarray(topk)
+    B, Hq, _ = q64.shape
+    P, Hkv = kc.shape[1], kc.shape[2]
+    group = Hq // Hkv
+    d_v = vc.shape[3]
+    o = np.zeros((B, Hq, d_v))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        L = int(ctx_lens[b])
+        if L <= 0:
+            continue
+        j = np.arange(L)
+        qb = (L - 1) // block
+        window = (j // block < sink) | (j // block > qb - local)
+        listed = np.zeros(L, dtype=bool)
+        t = topk[b]
+        listed[t[(t >= 0) & (t < L)]] = True
+        toks = j[window | listed]
+        pages = page_table[b, toks // P]
+        slots = toks % P
+        for g in range(Hkv):
+            kr = kc[pages, slots, g]                       # [T, d_qk]
+            vr = vc[pages, slots, g]                       # [T, d_v]
+            heads = slice(g * group, (g + 1) * group)
+            sc = scale * (kr @ q64[b, heads].T)            # [T, group]
+            m = sc.max(axis=0)
+            w = np.exp(sc - m)
+            o[b, heads] = (w.T @ vr) / w.sum(axis=0)[:, None]
+            lse[b, heads] = m + np.log(w.sum(axis=0))
+    return o, lse
+
+
 def backward(q, k, v, dout, *, block=128, sink=1, local=7, scale, full=False, rows=None):
     """Gradients of the prefill operator for the upstream gradient ``dout``.
 
