@@ -463,7 +463,7 @@ def bench_hybrid(iters: int):
     name = "hybrid_decode_bf16_latent_b32_h64_d576_L131072_sink16_win1024_top1024"
     res = {"workload": name, "us": ms * 1e3, "bytes": nbytes, "GB/s": gbs,
            "roofline": decode_roofline(gbs, [f"decode_split_latent grid={splits * B * 256}",
-                                             f"decode_merge<true, 512> grid={B * Hq * 64}"]),
+                                             f"decode_merge<true, 512> grid={B * Hq * 64} hybrid"]),
            "timing": f"HIP graph of {reps * n_inst} calls rotating over {n_inst} instances"}
     del graph, insts, outs, base, ws
     free_gpu()
