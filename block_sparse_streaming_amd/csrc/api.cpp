@@ -37,10 +37,18 @@ int elem_bytes(ssa_dtype t) { return t == SSA_BF16 ? 2 : 4; }
 
 bool dtype_ok(ssa_dtype t) { return t == SSA_F32 || t == SSA_BF16; }
 
+// The latent split kernel holds a whole CU (its ring of latent rows fills the
+// LDS): once a call has this many work-groups, wider splits cost no
+// parallelism and cut the fp32 partials each split writes and the merge
+// reads (64 heads x 512 x 4 B per split, about the size of 128 latent rows).
+constexpr int64_t kLatentTargetWgs = 256;
+
 // Work plan of a decode call; false if no compiled kernel fits the shape.
+// list_tokens: listed tokens per row (hybrid decode), which take splits of
+// the same width after the window's.
 bool make_plan(ssa_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t d_qk,
                int32_t d_v, int32_t page_size, int32_t max_pages, const ssa_pattern &pat, bool full,
-               DecodePlan *plan) {
+               DecodePlan *plan, int32_t list_tokens = 0) {
     const bool bf16 = dtype == SSA_BF16;
     const int group = heads_q / heads_kv;
     int chunk;
@@ -67,6 +75,11 @@ bool make_plan(ssa_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv
         const int64_t window = ((int64_t)pat.sink + pat.local) * pat.block;
         max_tokens = window < max_ctx ? window : max_ctx;
         split = kSsaSplitTokens;
+        if (plan->kind == ssa::kDecodeLatent) {
+            const int64_t rows = (int64_t)batch * heads_kv * plan->head_chunks;
+            auto wgs = [&](int64_t w) { return rows * ((max_tokens + w - 1) / w + (list_tokens + w - 1) / w); };
+            while (split < 1024 && wgs(2 * split) >= kLatentTargetWgs) split *= 2;
+        }
     }
     split = (split + chunk - 1) / chunk * chunk;
     if (plan->kind == ssa::kDecodeLatent) {
@@ -129,7 +142,8 @@ ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, co
     if ((d_qk * eb) % 16 || (d_v * eb) % 16) return SSA_ERR_INVALID_ARG;
 
     DecodePlan plan;
-    if (!make_plan(dtype, batch, heads_q, heads_kv, d_qk, d_v, page_size, max_pages, pattern, full, &plan))
+    if (!make_plan(dtype, batch, heads_q, heads_kv, d_qk, d_v, page_size, max_pages, pattern, full, &plan,
+                   topk_k))
         return SSA_ERR_UNSUPPORTED;
     if (topk_k > 0 && !add_list_splits(&plan, topk_k)) return SSA_ERR_UNSUPPORTED;
     if (plan.kind == ssa::kDecodeLatent) {
@@ -648,7 +662,7 @@ size_t hybrid_decode_workspace_size(ssa_dtype dtype, int32_t batch, int32_t head
         return 0;
     DecodePlan plan;
     if (!make_plan(dtype, batch, heads_q, heads_kv, d_qk, d_v, page_size, max_pages, pattern, false,
-                   &plan) ||
+                   &plan, topk_k) ||
         !add_list_splits(&plan, topk_k))
         return 0;
     return workspace_layout(batch, heads_q, d_v, plan).total;
