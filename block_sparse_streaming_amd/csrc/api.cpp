@@ -113,7 +113,8 @@ struct WorkspaceLayout {
 WorkspaceLayout workspace_layout(int32_t batch, int32_t heads_q, int32_t d_v, const DecodePlan &plan) {
     WorkspaceLayout w;
     const size_t slots = (size_t)batch * heads_q * plan.max_splits;
-    w.o_bytes = slots * d_v * sizeof(float);
+    // The latent kernel keeps its partial outputs in bf16, the others in fp32.
+    w.o_bytes = slots * d_v * (plan.kind == ssa::kDecodeLatent ? 2 : sizeof(float));
     w.lse_offset = (w.o_bytes + 255) / 256 * 256;
     w.total = w.lse_offset + slots * sizeof(float);
     return w;

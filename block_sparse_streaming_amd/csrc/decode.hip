@@ -550,9 +550,13 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     // o = 0 and lse = -inf, which the merge weights by zero.
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t slot = ((int64_t)bb * a.Hq + head) * a.plan.max_splits + split;
-    float *wo = a.ws_o + slot * kLatDv + 4 * kg;
+    // Partial outputs in bf16: per split they would otherwise weigh as much
+    // as the split's latent rows (64 heads x 512 x 4 B against 128 x 1152 B).
+    uint16_t *wo = (uint16_t *)a.ws_o + slot * kLatDv + 4 * kg;
 #pragma unroll
-    for (int d = 0; d < kLatDv / 16; ++d) *(f32x4 *)(wo + d * 16) = oacc[d] * inv;
+    for (int d = 0; d < kLatDv / 16; ++d)
+        *(u32x2 *)(wo + d * 16) = u32x2{pack_bf16x2(oacc[d][0] * inv, oacc[d][1] * inv),
+                                        pack_bf16x2(oacc[d][2] * inv, oacc[d][3] * inv)};
     if (kg == 0) a.ws_lse[slot] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
 }
 
@@ -588,7 +592,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
     }
     const int64_t slot0 = (int64_t)row * a.plan.max_splits;
     const float *wl = a.ws_lse + slot0;
-    const float *wo = a.ws_o + slot0 * D + E * lane;
+    // The latent split kernel (the only one with D = 512) stores its partial
+    // outputs in bf16; the others in fp32.
+    constexpr bool kPartBF16 = D == 512;
+    using Part = std::conditional_t<kPartBF16, uint16_t, float>;
+    const Part *wo = (const Part *)a.ws_o + slot0 * D + E * lane;
 
     // Partial rows of splits s0 .. s0+7 (clamped to the last split).
     float part[kMergeBatch][E];
@@ -596,8 +604,16 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
 #pragma unroll
         for (int u = 0; u < kMergeBatch; ++u) {
             const int s = s0 + u < nb ? s0 + u : nb - 1;
-            const float *src = wo + (int64_t)s * D;
-            if constexpr (E >= 4) {
+            const Part *src = wo + (int64_t)s * D;
+            if constexpr (kPartBF16) {
+                static_assert(E == 8, "bf16 partials: 8 per lane");
+                const u32x4 v = *(const u32x4 *)src;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    part[u][2 * e] = bf16_lo(v[e]);
+                    part[u][2 * e + 1] = bf16_hi(v[e]);
+                }
+            } else if constexpr (E >= 4) {
 #pragma unroll
                 for (int e4 = 0; e4 < E / 4; ++e4) {
                     const f32x4 v = *(const f32x4 *)(src + 4 * e4);

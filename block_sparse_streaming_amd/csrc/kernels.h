@@ -97,7 +97,7 @@ struct DecodeArgs {
     float scale_log2;
     void *o;
     float *lse;                     // [B, Hq] or null
-    float *ws_o;                    // [B, Hq, max_splits, d_v]
+    float *ws_o;                    // [B, Hq, max_splits, d_v]; bf16 for the latent kernel
     float *ws_lse;                  // [B, Hq, max_splits], log2 domain
     DecodePlan plan;
     // Several query rows per sequence: B counts query rows, and row r reads

@@ -106,10 +106,11 @@ def test_decode_validation(full):
 def test_workspace_sizes():
     import torch
     ws = ssa.decode_workspace_size
-    # windowed decode: (s + l) * b / 128 tokens per split = 8 splits of (d_v + 1) floats
+    # windowed latent decode: (s + l) * b / 128 tokens per split = 8 splits,
+    # each a bf16 partial output of d_v values and an fp32 lse
     slots = 32 * 64 * 8
     need = ws(torch.bfloat16, 32, 64, 1, 576, 512, 128, 1024)
-    lse_off = -(-slots * 512 * 4 // 256) * 256
+    lse_off = -(-slots * 512 * 2 // 256) * 256
     assert need == lse_off + slots * 4
     # short caches bound the window: max_pages * page_size = 256 tokens -> 2 splits
     assert ws(torch.bfloat16, 1, 16, 16, 128, 128, 128, 2) == -(-16 * 2 * 128 * 4 // 256) * 256 + 16 * 2 * 4
@@ -119,7 +120,7 @@ def test_workspace_sizes():
     # (at most (480 - 2) // 2 + 4 = 243 pages), so 262144 tokens need 547 splits
     slots = 4 * 64 * 547
     assert ws(torch.bfloat16, 4, 64, 1, 576, 512, 2, 131072, full=True) == \
-        -(-slots * 512 * 4 // 256) * 256 + slots * 4
+        -(-slots * 512 * 2 // 256) * 256 + slots * 4
     assert ws(torch.bfloat16, 1, 4, 3, 128, 128, 128, 8) == 0          # invalid heads
     assert ws(torch.bfloat16, 1, 4, 4, 128, 128, 128, 8, local=0) == 0
 
