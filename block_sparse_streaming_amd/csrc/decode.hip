@@ -267,6 +267,7 @@ constexpr int kLatCh = 32;                            // latent rows per LDS buf
 constexpr int kLatUnits = kLatDqk / 8;                // 16-byte units per row
 constexpr int kLatThreads = 256;
 constexpr int kLatBufs = 4;                           // ring depth
+constexpr int kLatLead = 3;                           // LDS operands read this many MFMAs ahead
 constexpr int kLatRowsPerWave = kLatCh / 4;           // rows each wave transfers per chunk
 constexpr int kLatDma = kLatRowsPerWave * kLatUnits / 64;  // transfers per wave per chunk
 constexpr int kLatMaxPages = kDecodeLatentMaxPages;   // page ids of one split kept in LDS
@@ -436,14 +437,23 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
         const char *rowp = (const char *)buf + kl;
         s[0] = f32x4{0.f, 0.f, 0.f, 0.f};
         s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // One wave per SIMD: an operand read just before its MFMA exposes the
+        // whole LDS latency, so operands are read kLatLead MFMAs ahead (the
+        // fences keep the compiler from regrouping reads and waits).
+        constexpr int NS = 2 * (kLatDqk / 32);  // MFMA n: ks = n / 2, token block n % 2
+        bf16x8 kf[NS];
+        auto load = [&](int n) __attribute__((always_inline)) {
+            const int ks = n >> 1, tb = n & 1;
+            kf[n] = *(const bf16x8 *)(rowp + tb * 16 * (kLatDqk * 2) + 128 * (ks >> 1) + ((ks & 1) ? ko : ke));
+        };
 #pragma unroll
-        for (int ks = 0; ks < kLatDqk / 32; ++ks)
+        for (int n = 0; n < kLatLead; ++n) load(n);
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                const bf16x8 kf = *(const bf16x8 *)(rowp + tb * 16 * (kLatDqk * 2) + 128 * (ks >> 1) +
-                                                    ((ks & 1) ? ko : ke));
-                s[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[tb], 0, 0, 0);
-            }
+        for (int n = 0; n < NS; ++n) {
+            if (n + kLatLead < NS) load(n + kLatLead);
+            __builtin_amdgcn_sched_barrier(0);
+            s[n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[n], qf[n >> 1], s[n & 1], 0, 0, 0);
+        }
         const int nvalid = ntok - c * kLatCh;
         const uint32_t vm = listed ? vmask[c % kLatBufs] : 0xffffffffu;
 #pragma unroll
@@ -500,13 +510,21 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
             asm volatile("" : "+v"(vl[q4]));
         }
         const char *cb = (const char *)buf;
-#pragma unroll
-        for (int d = 0; d < kLatDv / 16; ++d) {
+        constexpr int NO = kLatDv / 16;
+        bf16x8 vf[NO];
+        auto vload = [&](int d) __attribute__((always_inline)) {
             const char *vp = cb + vl[d & 3] + 128 * (d >> 2);
             const i16x4 lo = lds_read_tr16(vp);
             const i16x4 up = lds_read_tr16(vp + 16 * (kLatDqk * 2));
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[d], 0, 0, 0);
+            vf[d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+#pragma unroll
+        for (int d = 0; d < kLatLead; ++d) vload(d);
+#pragma unroll
+        for (int d = 0; d < NO; ++d) {
+            if (d + kLatLead < NO) vload(d + kLatLead);
+            __builtin_amdgcn_sched_barrier(0);
+            oacc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[d], pf, oacc[d], 0, 0, 0);
         }
     };
 
