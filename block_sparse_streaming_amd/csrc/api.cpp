@@ -97,9 +97,8 @@ bool make_plan(ssa_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv
 }
 
 // Hybrid decode: the listed tokens take splits of the same size after the
-// window's. Only the latent kernel reads a token list.
+// window's (both split kernels read a token list).
 bool add_list_splits(DecodePlan *plan, int32_t topk_k) {
-    if (plan->kind != ssa::kDecodeLatent) return false;
     const int64_t n = plan->max_splits + ((int64_t)topk_k + plan->split_tokens - 1) / plan->split_tokens;
     if (n > 65535) return false;
     plan->max_splits = (int)n;

@@ -117,7 +117,10 @@ __device__ __forceinline__ float slice_elem(const RowSlice<Elem, E> &r, int e) {
 // whose rows are all requested at once; the next chunk's page ids are read
 // while this chunk's rows are in flight. Each lane keeps its own online
 // softmax state, and the token groups are merged through LDS at the end.
-template <bool kBF16, int D, int G>
+// kList: the call has listed tokens (hybrid decode); without them the
+// window-only path keeps no per-token state between the page-id read and the
+// row read.
+template <bool kBF16, int D, int G, bool kList>
 __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeArgs a) {
     using Elem = std::conditional_t<kBF16, uint16_t, float>;
     constexpr int E = D / kTpt;
@@ -133,26 +136,60 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
     const int64_t L = row_context(a, bb);
     if (L <= 0) return;
     const Sel sel = select_tokens(L, a);
-    const int64_t p_begin = (int64_t)split * a.plan.split_tokens;
-    if (p_begin >= sel.total) return;
-    const int64_t p_end = p_begin + a.plan.split_tokens < sel.total ? p_begin + a.plan.split_tokens
-                                                                      : sel.total;
+    // Splits [0, n_win) cover the window's positions; the next list_splits(a)
+    // cover the listed tokens (hybrid decode), positions of the list.
+    const int n_win = (int)((sel.total + a.plan.split_tokens - 1) / a.plan.split_tokens);
+    const bool listed = kList && split >= n_win;
+    const int64_t p_begin = (int64_t)(listed ? split - n_win : split) * a.plan.split_tokens;
+    const int64_t p_lim = listed ? (int64_t)a.topk_k : sel.total;
+    if (p_begin >= p_lim) return;
+    const int64_t p_end = p_begin + a.plan.split_tokens < p_lim ? p_begin + a.plan.split_tokens : p_lim;
     // Positions and tokens fit in 32 bits (context lengths are int32).
     const uint32_t up_end = (uint32_t)p_end, ur1 = (uint32_t)sel.r1_end, ur2 = (uint32_t)sel.r2_begin;
     const uint32_t uP = (uint32_t)a.page_size;
-    const int32_t *ptab = a.page_table + row_sequence(a, bb) * a.max_pages;
-
-    // Token of lane group tg's u-th position in the chunk starting at c0
-    // (clamped to the split's last position; masked later).
-    auto token_of = [&](uint32_t c0, int u) __attribute__((always_inline)) -> uint32_t {
+    const int64_t seq = row_sequence(a, bb);
+    const int32_t *ptab = a.page_table + seq * a.max_pages;
+    const uint32_t uL = (uint32_t)L, ur2end = ur2 < uL ? ur2 : uL;
+    // Token of a window position (clamped to the split's last position).
+    auto window_token = [&](uint32_t c0, int u) __attribute__((always_inline)) -> uint32_t {
         uint32_t pp = c0 + (uint32_t)(tg + kGroups * u);
         pp = pp < up_end ? pp : up_end - 1;
         return pp < ur1 ? pp : ur2 + (pp - ur1);
     };
+
+    // Token of lane group tg's u-th position in the chunk starting at c0
+    // (clamped to the split's last position; masked later). A listed token
+    // inside the window, past the context or negative is skipped: token 0
+    // stands in for it and its bit in `ok` is clear.
+    auto token_of = [&](uint32_t c0, int u, bool &ok) __attribute__((always_inline)) -> uint32_t {
+        if (!listed) {
+            ok = true;
+            return window_token(c0, u);
+        }
+        uint32_t pp = c0 + (uint32_t)(tg + kGroups * u);
+        pp = pp < up_end ? pp : up_end - 1;
+        const int t0 = a.topk[seq * a.topk_k + pp];
+        ok = t0 >= (int)ur1 && (uint32_t)t0 < ur2end;
+        return ok ? (uint32_t)t0 : 0u;
+    };
+    // Page ids of the next chunk, and with a list its tokens and attended bits.
     int32_t pid[kTpl];
+    uint32_t tok_next[kList ? kTpl : 1];
+    uint32_t ok_next = 0xffffffffu;
     auto load_pids = [&](uint32_t c0) __attribute__((always_inline)) {
+        if constexpr (kList) {
+            ok_next = 0;
 #pragma unroll
-        for (int u = 0; u < kTpl; ++u) pid[u] = ptab[token_of(c0, u) / uP];
+            for (int u = 0; u < kTpl; ++u) {
+                bool ok;
+                tok_next[u] = token_of(c0, u, ok);
+                ok_next |= (ok ? 1u : 0u) << u;
+                pid[u] = ptab[tok_next[u] / uP];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kTpl; ++u) pid[u] = ptab[window_token(c0, u) / uP];
+        }
     };
     Slice kr[kTpl], vr[kTpl];
     const Elem *kc = (const Elem *)a.kc + g * a.ks[2] + tl * E;
@@ -160,7 +197,9 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
     auto load_rows = [&](uint32_t c0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < kTpl; ++u) {
-            const uint32_t tok = token_of(c0, u);
+            uint32_t tok;
+            if constexpr (kList) tok = tok_next[u];
+            else tok = window_token(c0, u);
             const int64_t slot = (int64_t)(tok % uP);
             load_slice<Elem, E>(kc + pid[u] * a.ks[0] + slot * a.ks[1], kr[u]);
             load_slice<Elem, E>(vc + pid[u] * a.vs[0] + slot * a.vs[1], vr[u]);
@@ -190,6 +229,7 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
 
     for (uint32_t c0 = c_first; c0 < up_end; c0 += kChunk) {
         load_rows(c0);
+        const uint32_t ok_cur = ok_next;
         if (c0 + kChunk < up_end) load_pids(c0 + kChunk);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
@@ -203,7 +243,7 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
                 d += __shfl_xor(d, 4);
                 d += __shfl_xor(d, 2);
                 d += __shfl_xor(d, 1);
-                s[u] = c0 + (uint32_t)(tg + kGroups * u) < up_end ? d : -INFINITY;
+                s[u] = (c0 + (uint32_t)(tg + kGroups * u) < up_end && ((ok_cur >> u) & 1u)) ? d : -INFINITY;
             }
             float mx = m[hh];
 #pragma unroll
@@ -253,8 +293,10 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
             O += w * sm_o[q][hh][d];
         }
         const int64_t slot = ((int64_t)bb * a.Hq + g * G + hh) * a.plan.max_splits + split;
-        a.ws_o[slot * D + d] = O / Z;
-        if (d == 0) a.ws_lse[slot] = M + log2f(Z);
+        // A split with no attended key (all of its listed tokens skipped):
+        // o = 0 and lse = -inf, which the merge weights by zero.
+        a.ws_o[slot * D + d] = Z > 0.f ? O / Z : 0.f;
+        if (d == 0) a.ws_lse[slot] = Z > 0.f ? M + log2f(Z) : -INFINITY;
     }
 }
 
@@ -694,7 +736,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
 template <bool kBF16, int D, int G>
 hipError_t launch_valu(const DecodeArgs &a, hipStream_t stream) {
     void *args[] = {(void *)&a};
-    return hipLaunchKernel((const void *)decode_split_valu<kBF16, D, G>,
+    const void *k = a.topk_k > 0 ? (const void *)decode_split_valu<kBF16, D, G, true>
+                                 : (const void *)decode_split_valu<kBF16, D, G, false>;
+    return hipLaunchKernel(k,
                            dim3(a.plan.max_splits, a.Hkv, a.B), dim3(kValuThreads), args, 0, stream);
 }
 

@@ -308,9 +308,10 @@ size_t ssa_extend_workspace_size(ssa_dtype dtype, int32_t batch, int32_t total_q
  *              token would count twice). Trusted device data.
  *   workspace  at least hybrid_decode_workspace_size(...) bytes.
  * The window and the listed tokens are cut into splits of one size; one
- * merge combines all of a row's splits. Compiled: the bf16 latent shape
- * (d_qk = 576, d_v = 512, heads_q / heads_kv a multiple of 16); other shapes
- * return SSA_ERR_UNSUPPORTED. topk_k must be >= 1.
+ * merge combines all of a row's splits. Compiled: every shape ssa_decode
+ * compiles (bf16 or fp32 with d_qk = d_v in {64, 128, 256} and heads_q /
+ * heads_kv in {1, 2, 4, 8}; the bf16 latent shape). The list is shared by a
+ * sequence's query heads. topk_k must be >= 1.
  */
 ssa_status hybrid_decode(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
                          const int64_t k_strides[3], const int64_t v_strides[3],

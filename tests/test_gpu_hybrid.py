@@ -1,6 +1,7 @@
 """GPU parity of hybrid_decode (SSA window plus listed tokens, merged by
 log-sum-exp) against the CPU oracle, through the C ABI, on the latent decode
-shape. The oracle reads only the pages of the window and of the listed
+shape (MFMA split kernel) and on MHA / GQA shapes in bf16 and fp32 (VALU split
+kernel). The oracle reads only the pages of the window and of the listed
 tokens; every other page is NaN, so a wrong page read would show. Lists are
 distinct positions drawn from the whole context: entries that fall inside the
 window are skipped by the kernel and absorbed by the oracle's union; padding
@@ -30,27 +31,31 @@ def _needed_pages(L, lst, P, b, s, l):
     return np.unique(j[keep] // P)
 
 
-def _case(lens, K, Hq, pattern, seed, *, page_size=inputs.PAGE_SIZE, pad=0, extra=None, rows=None):
-    inp = inputs.extend_inputs(lens, (1,) * len(lens), Hq, 1, LAT_DQK, LAT_DV, torch.bfloat16, DEV, seed,
-                               page_size=page_size, latent=True, spare_pages=2)
+def _case(lens, K, Hq, pattern, seed, *, page_size=inputs.PAGE_SIZE, pad=0, extra=None, rows=None,
+          Hkv=1, dqk=LAT_DQK, dv=LAT_DV, dtype=torch.bfloat16):
+    latent = dqk == LAT_DQK
+    inp = inputs.extend_inputs(lens, (1,) * len(lens), Hq, Hkv, dqk, dv, dtype, DEV, seed,
+                               page_size=page_size, latent=latent, spare_pages=2)
     lst = inputs.token_lists(lens, K, seed + 1, pad_per_row=pad)
     if extra is not None:
         lst = np.concatenate([lst, extra], axis=1)
     topk = torch.from_numpy(lst).to(DEV)
-    scale = LAT_DQK ** -0.5
-    say("hybrid", "lens", lens[:6], len(lens), "K", lst.shape[1], "Hq", Hq, pattern, "page", page_size)
+    scale = dqk ** -0.5
+    say("hybrid", "lens", lens[:6], len(lens), "K", lst.shape[1], "Hq", Hq, "Hkv", Hkv, "d", dqk, dv, dtype,
+        pattern, "page", page_size)
     o, lse = ssa.hybrid_decode(inp.q, inp.k_cache, inp.v_cache, inp.page_table, inp.ctx_lens, topk,
                                **pattern, scale=scale, return_lse=True)
     torch.cuda.synchronize()
     rows = np.arange(len(lens)) if rows is None else np.asarray(rows)
     need = [_needed_pages(lens[b], lst[b], page_size, pattern["block"], pattern["sink"], pattern["local"])
             if b in set(rows.tolist()) else np.zeros(0, np.int64) for b in range(len(lens))]
-    kc, vc, table = compact_pages(inp.k_cache, inp.v_cache, inp.table_np, need, latent_dv=LAT_DV)
+    kc, vc, table = compact_pages(inp.k_cache, inp.v_cache, inp.table_np, need,
+                                  latent_dv=LAT_DV if latent else None)
     ro, rl = oracle.hybrid_decode(host(inp.q)[rows], kc, vc, table[rows], np.array(lens)[rows],
                                   lst[rows], **pattern, scale=scale)
     idx = torch.as_tensor(rows, device=DEV)
-    assert_parity(o[idx], ro, torch.bfloat16, "hybrid")
-    assert_lse(lse[idx], rl, torch.bfloat16, "hybrid lse")
+    assert_parity(o[idx], ro, dtype, "hybrid")
+    assert_lse(lse[idx], rl, dtype, "hybrid lse")
     return o, lse
 
 
@@ -115,3 +120,22 @@ def test_full_size_workload_sampled():
     LSA budget; four sampled sequences against the oracle."""
     lens = (inputs.EXTEND_MTP_LEN,) * 32
     _case(lens, inputs.HYBRID_K, 64, inputs.HYBRID_PATTERN, seed=inputs.HYBRID_SEED, rows=[0, 7, 19, 31])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("Hq,Hkv,d", [(4, 4, 128), (8, 2, 64), (8, 2, 256), (16, 2, 128)])
+def test_mha_gqa_shapes(dtype, Hq, Hkv, d):
+    """The VALU split kernel with a list: GQA groups 1, 4 and 8, head dims 64,
+    128 and 256, bf16 and fp32, contexts around and beyond the window, a
+    half-padded list with skipped entries."""
+    if Hq // Hkv == 8 and d == 256:
+        pytest.skip("no compiled variant (group * d_v > 1024)")
+    lens = (1, 1040, 1041, 3000, 20000)
+    extra = np.array([[0, 1, 5, -1], [3, 1039, 1040, -1], [1040, 2000, 17, -9], [2999, 3000, 16, 15],
+                      [19999, 5, 10 ** 6, -1]], np.int32)
+    _case(lens, 300, Hq, inputs.HYBRID_PATTERN, seed=970 + Hq + d, pad=50, extra=extra, Hkv=Hkv, dqk=d, dv=d,
+          dtype=dtype)
+
+
+def test_mha_ssa_window_with_list():
+    _case((7000, 300, 20000), 512, 4, dict(block=128, sink=1, local=7), seed=980, Hkv=4, dqk=128, dv=128)
