@@ -148,12 +148,11 @@ def free_gpu():
 # ---------------------------------------------------------------------------
 # Prefill
 # ---------------------------------------------------------------------------
-def prefill_setup(cfg_id: int):
+def prefill_setup(cfg):
     import torch
     import block_sparse_streaming_amd as ssa
     from block_sparse_streaming_amd import inputs
 
-    cfg = inputs.CONFIGS[cfg_id]
     q, k, v = inputs.prefill_inputs(cfg, "cuda:0")
     out = torch.empty((cfg.B, cfg.N, cfg.Hq, cfg.d_v), dtype=cfg.dtype, device="cuda:0")
 
@@ -163,11 +162,11 @@ def prefill_setup(cfg_id: int):
     return cfg, step
 
 
-def bench_prefill(cfg_id: int, steps: int, warmup: int):
+def bench_prefill(cfg, steps: int, warmup: int):
     import torch
     from block_sparse_streaming_amd import inputs
 
-    cfg, step = prefill_setup(cfg_id)
+    cfg, step = prefill_setup(cfg)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -196,12 +195,11 @@ def bench_prefill(cfg_id: int, steps: int, warmup: int):
 DUAL_ALPHA = 0.5
 
 
-def dual_setup(cfg_id: int):
+def dual_setup(cfg):
     import torch
     import block_sparse_streaming_amd as ssa
     from block_sparse_streaming_amd import inputs
 
-    cfg = inputs.CONFIGS[cfg_id]
     q, k, v = inputs.prefill_inputs(cfg, "cuda:0")
     outs = tuple(torch.empty((cfg.B, cfg.N, cfg.Hq, cfg.d_v), dtype=cfg.dtype, device="cuda:0")
                  for _ in range(3))
@@ -212,12 +210,12 @@ def dual_setup(cfg_id: int):
     return cfg, step
 
 
-def bench_dual(cfg_id: int, steps: int, warmup: int):
+def bench_dual(cfg, steps: int, warmup: int):
     """ssa_prefill_dual: the SSA output, the full causal output and their mix
     in one launch. Its work is that of full causal attention: N(N+1)/2 pairs
     per head at 2 (d_qk + d_v) flops each."""
     import torch
-    cfg, step = dual_setup(cfg_id)
+    cfg, step = dual_setup(cfg)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -503,12 +501,11 @@ def backward_kernel_keys(cfg) -> list[str]:
             f"ssa_bwd_sink_finalize{d} grid={fin * 256}"]
 
 
-def backward_setup(cfg_id: int):
+def backward_setup(cfg):
     import torch
     import block_sparse_streaming_amd as ssa
     from block_sparse_streaming_amd import inputs
 
-    cfg = inputs.CONFIGS[cfg_id]
     q, k, v = inputs.prefill_inputs(cfg, "cuda:0")
     do = inputs.prefill_grad(cfg, "cuda:0")
     o, lse = ssa.prefill(q, k, v, **inputs.PATTERN, scale=cfg.scale, return_lse=True)
@@ -524,11 +521,11 @@ def backward_setup(cfg_id: int):
     return cfg, step
 
 
-def bench_backward(cfg_id: int, steps: int, warmup: int):
+def bench_backward(cfg, steps: int, warmup: int):
     """ssa_prefill_backward (three launches: dq, dk/dv, sink finalize) on a
     prefill workload, given the forward's o and lse."""
     import torch
-    cfg, step = backward_setup(cfg_id)
+    cfg, step = backward_setup(cfg)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -573,7 +570,7 @@ def bench_decode_latent(iters: int):
     import block_sparse_streaming_amd as ssa
     from block_sparse_streaming_amd import inputs
 
-    cfg = inputs.CONFIGS[3]
+    cfg = inputs.DECODE_LATENT_128K
     pat = inputs.PATTERN
     dev = "cuda:0"
     base = inputs.decode_inputs(cfg, dev)
@@ -653,7 +650,7 @@ def bench_decode_ragged(iters: int):
     import block_sparse_streaming_amd as ssa
     from block_sparse_streaming_amd import inputs
 
-    cfg = inputs.CONFIGS[5]
+    cfg = inputs.DECODE_RAGGED
     pat = inputs.PATTERN
     dev = "cuda:0"
     inp = inputs.decode_inputs(cfg, dev)
@@ -692,7 +689,7 @@ def cpu_baseline():
     import oracle
     from block_sparse_streaming_amd import inputs
 
-    cfg = inputs.CONFIGS[2]
+    cfg = inputs.PREFILL_BF16_32K
     pat = inputs.PATTERN
     gen = torch.Generator().manual_seed(cfg.seed)
     q = torch.randn((1, cfg.N, cfg.Hq, cfg.d_qk), generator=gen).to(cfg.dtype)
@@ -714,18 +711,19 @@ def cpu_baseline():
 # ---------------------------------------------------------------------------
 def profile_run(what: str):
     import torch
+    from block_sparse_streaming_amd import inputs
     if what == "prefill":
-        _, step = prefill_setup(2)
+        _, step = prefill_setup(inputs.PREFILL_BF16_32K)
         for _ in range(3):
             step()
     elif what == "decode":
         bench_decode_latent(64)
     elif what == "backward":
-        _, step = backward_setup(2)
+        _, step = backward_setup(inputs.PREFILL_BF16_32K)
         for _ in range(3):
             step()
     elif what == "dual":
-        _, step = dual_setup(2)
+        _, step = dual_setup(inputs.PREFILL_BF16_32K)
         for _ in range(3):
             step()
     elif what == "hybrid":
@@ -754,8 +752,9 @@ def main():
                     help="time only the 32K prefill (and the CPU oracle)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards with no communication; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path "
+              "shards by head or by sequence with no communication, so one GPU's share is the "
+              "measured workload", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -773,12 +772,13 @@ def main():
         m = measure_ceilings()
         note(f"measured ceilings: bf16 GEMM {m['bf16_gemm_tflops']:.0f} TFLOP/s, "
              f"HBM read {m['hbm_read_gbs']:.0f} GB/s")
-    cfg, head = bench_prefill(2, args.steps, args.warmup)
+    from block_sparse_streaming_amd import inputs
+    cfg, head = bench_prefill(inputs.PREFILL_BF16_32K, args.steps, args.warmup)
     note(f"prefill {cfg.name}: {head['ms']:.4f} ms/launch, {head['TFLOP/s']:.1f} TFLOP/s")
     workloads = {}
     if not args.headline_only:
-        for cid, steps in ((1, 50), (4, 5)):
-            c, r = bench_prefill(cid, steps, 2)
+        for wl, steps in ((inputs.PREFILL_FP32_2K, 50), (inputs.PREFILL_BF16_256K, 5)):
+            c, r = bench_prefill(wl, steps, 2)
             workloads[c.name] = r
             note(f"prefill {c.name}: {r['ms']:.4f} ms/launch, {r['TFLOP/s']:.1f} TFLOP/s")
         dec = bench_decode_latent(256)
@@ -790,11 +790,11 @@ def main():
         workloads[rag["workload"]] = rag
         note(f"decode {rag['workload']}: ssa {rag['ssa_decode']['us']:.2f} us "
              f"({rag['ssa_decode']['GB/s']:.0f} GB/s)")
-        for cid, steps in ((2, 20), (4, 3)):
-            name, r = bench_backward(cid, steps, 2)
+        for wl, steps in ((inputs.PREFILL_BF16_32K, 20), (inputs.PREFILL_BF16_256K, 3)):
+            name, r = bench_backward(wl, steps, 2)
             workloads[name] = r
             note(f"backward {name}: {r['ms']:.4f} ms/call, {r['TFLOP/s']:.1f} TFLOP/s")
-        name, r = bench_dual(2, 10, 2)
+        name, r = bench_dual(inputs.PREFILL_BF16_32K, 10, 2)
         workloads[name] = r
         note(f"dual {name}: {r['ms']:.4f} ms/launch, {r['TFLOP/s']:.1f} TFLOP/s")
         name, r = bench_extend_chunk(10, 2)

@@ -66,7 +66,7 @@ class DecodeConfig:
         return 1.0 / math.sqrt(self.d_qk)
 
 
-def config5_lens(seed: int = 1005) -> tuple:
+def ragged_lens(seed: int = 1005) -> tuple:
     """64 context lengths floor(exp(U(ln 4096, ln 1048576))) plus one in [1, 1023]."""
     rng = np.random.default_rng(seed)
     u = rng.uniform(math.log(4096), math.log(1048576), size=64)
@@ -75,16 +75,18 @@ def config5_lens(seed: int = 1005) -> tuple:
     return tuple(lens)
 
 
-CONFIGS = {
-    1: PrefillConfig("prefill_fp32_b1_n2048_h4_d64", torch.float32, 1, 2048, 4, 4, 64, 64, 1001),
-    2: PrefillConfig("prefill_bf16_b1_n32768_h16_d128", torch.bfloat16, 1, 32768, 16, 16, 128, 128, 1002),
-    3: DecodeConfig("decode_bf16_latent_b32_h64_d576_L131072", torch.bfloat16, 64, 1, 576, 512, True,
-                    1003, lens=(131072,) * 32),
-    4: PrefillConfig("prefill_bf16_b1_n262144_h64_dqk192_dv128", torch.bfloat16, 1, 262144, 64, 64,
-                     192, 128, 1004),
-    5: DecodeConfig("decode_bf16_ragged_65seq_h16_d128", torch.bfloat16, 16, 16, 128, 128, False, 1005,
-                    lens=config5_lens()),
-}
+# The workloads, each named by its shape.
+PREFILL_FP32_2K = PrefillConfig("prefill_fp32_b1_n2048_h4_d64", torch.float32, 1, 2048, 4, 4, 64, 64, 1001)
+PREFILL_BF16_32K = PrefillConfig("prefill_bf16_b1_n32768_h16_d128", torch.bfloat16, 1, 32768, 16, 16, 128,
+                                 128, 1002)
+DECODE_LATENT_128K = DecodeConfig("decode_bf16_latent_b32_h64_d576_L131072", torch.bfloat16, 64, 1, 576, 512,
+                                  True, 1003, lens=(131072,) * 32)
+PREFILL_BF16_256K = PrefillConfig("prefill_bf16_b1_n262144_h64_dqk192_dv128", torch.bfloat16, 1, 262144, 64,
+                                  64, 192, 128, 1004)
+DECODE_RAGGED = DecodeConfig("decode_bf16_ragged_65seq_h16_d128", torch.bfloat16, 16, 16, 128, 128, False,
+                             1005, lens=ragged_lens())
+WORKLOADS = {c.name: c for c in (PREFILL_FP32_2K, PREFILL_BF16_32K, DECODE_LATENT_128K, PREFILL_BF16_256K,
+                                 DECODE_RAGGED)}
 
 
 def randn(shape, dtype: torch.dtype, device, gen: torch.Generator, chunk_elems: int = 1 << 28):

@@ -179,11 +179,11 @@ def _sampled_full_size(cfg, q_tiles, k_tiles, heads):
 def test_full_size_32k_sampled():
     """The 32K, 16-head, d=128 workload in the launch configuration the
     benchmark times."""
-    _sampled_full_size(inputs.CONFIGS[2], q_tiles=[0, 1, 7, 8, 131, 255],
+    _sampled_full_size(inputs.PREFILL_BF16_32K, q_tiles=[0, 1, 7, 8, 131, 255],
                        k_tiles=[1, 2, 100, 250, 255], heads=[0, 15])
 
 
 def test_full_size_256k_sampled():
     """The 256K, 64-head, d_qk=192 / d_v=128 workload."""
-    _sampled_full_size(inputs.CONFIGS[4], q_tiles=[0, 8, 1024, 2047],
+    _sampled_full_size(inputs.PREFILL_BF16_256K, q_tiles=[0, 8, 1024, 2047],
                        k_tiles=[1, 1023, 2047], heads=[0, 63])

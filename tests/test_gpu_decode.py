@@ -116,7 +116,7 @@ def test_latent_tiny_pages_wide_table(page_size):
 def test_config3_latent_full_size():
     """32 sequences x 131072 tokens, shuffled pages: SSA decode on every
     sequence, full decode on two of them (the oracle's cost is the limit)."""
-    cfg = inputs.CONFIGS[3]
+    cfg = inputs.DECODE_LATENT_128K
     inp = inputs.decode_inputs(cfg, DEV)
     _check(cfg, inp, PAT, what=cfg.name)
     sub = [0, 17]
@@ -128,7 +128,7 @@ def test_config3_latent_full_size():
 
 
 def test_config5_ragged_full_size():
-    cfg = inputs.CONFIGS[5]
+    cfg = inputs.DECODE_RAGGED
     inp = inputs.decode_inputs(cfg, DEV)
     assert min(inp.lens) < 1024
     _check(cfg, inp, PAT, what=cfg.name)

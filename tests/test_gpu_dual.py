@@ -120,7 +120,7 @@ def test_full_size_32k_sampled():
     """The 32K, 16-head, d=128 workload: sampled query tiles of two heads
     against the oracle, every row checked for the mix and for the SSA half
     matching the plain forward bit for bit."""
-    cfg = inputs.CONFIGS[2]
+    cfg = inputs.PREFILL_BF16_32K
     q, k, v = inputs.prefill_inputs(cfg, DEV)
     alpha = 0.375
     say("dual full size", cfg.name)

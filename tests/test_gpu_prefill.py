@@ -40,7 +40,7 @@ def _run_and_check(q, k, v, pattern, scale, rows=None, what=""):
 
 
 def test_config1_fp32_full():
-    cfg = inputs.CONFIGS[1]
+    cfg = inputs.PREFILL_FP32_2K
     q, k, v = inputs.prefill_inputs(cfg, DEV)
     _run_and_check(q, k, v, inputs.PATTERN, cfg.scale, what=cfg.name)
 
@@ -103,7 +103,7 @@ def _sample_tiles(num_tiles, fixed, n_random, seed):
 
 
 def test_config2_sampled_tiles():
-    cfg = inputs.CONFIGS[2]
+    cfg = inputs.PREFILL_BF16_32K
     q, k, v = inputs.prefill_inputs(cfg, DEV)
     tiles = _sample_tiles(cfg.N // 128, [0, 1, 6, 7, 8, 9, 128, 255], 6, 2)
     rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in tiles])
@@ -112,7 +112,7 @@ def test_config2_sampled_tiles():
 
 def test_config4_stratified_sample():
     """Every head; query blocks 0..8, 1023, 1024, 2047 and 8 seeded random blocks."""
-    cfg = inputs.CONFIGS[4]
+    cfg = inputs.PREFILL_BF16_256K
     q, k, v = inputs.prefill_inputs(cfg, DEV)
     tiles = _sample_tiles(cfg.N // 128, list(range(9)) + [1023, 1024, 2047], 8, 4)
     rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in tiles])
