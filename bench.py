@@ -369,8 +369,8 @@ def bench_extend_mtp(iters: int):
     name = "extend_mtp_bf16_latent_b32_q4_h64_d576_L131072"
     res = {"workload": name, "us": ms * 1e3, "bytes": nbytes, "GB/s": gbs,
            "rows_per_call": rows,
-           "roofline": decode_roofline(gbs, [f"decode_split_latent grid={8 * B * T * 256}",
-                                             f"decode_merge<true, 512> grid={rows * Hq * 64}"]),
+           "roofline": decode_roofline(gbs, ["extend_rows mtp", "decode_split_latent mtp",
+                                             "decode_merge<true, 512> mtp"]),
            "timing": f"HIP graph of {reps * n_inst} calls rotating over {n_inst} instances"}
     del graph, insts, outs, base, ws
     free_gpu()
@@ -457,11 +457,10 @@ def bench_hybrid(iters: int):
     nbytes = int(np.mean([hybrid_bytes(base.lens, inst[3], **pat, page_size=inputs.PAGE_SIZE, Hq=Hq)
                           for inst in insts]))
     gbs = nbytes / (ms * 1e-3) / 1e9
-    splits = 17  # 1,040 window tokens and 1,024 listed ones in splits of 128
     name = "hybrid_decode_bf16_latent_b32_h64_d576_L131072_sink16_win1024_top1024"
     res = {"workload": name, "us": ms * 1e3, "bytes": nbytes, "GB/s": gbs,
-           "roofline": decode_roofline(gbs, [f"decode_split_latent grid={splits * B * 256}",
-                                             f"decode_merge<true, 512> grid={B * Hq * 64} hybrid"]),
+           "roofline": decode_roofline(gbs, ["decode_split_latent hybrid",
+                                             "decode_merge<true, 512> hybrid"]),
            "timing": f"HIP graph of {reps * n_inst} calls rotating over {n_inst} instances"}
     del graph, insts, outs, base, ws
     free_gpu()
@@ -629,12 +628,12 @@ def bench_decode_latent(iters: int):
     res = {
         "workload": cfg.name,
         "ssa_decode": {"us": ssa_ms * 1e3, "bytes": ssa_bytes, "GB/s": ssa_gbs,
-                       "roofline": decode_roofline(ssa_gbs, ["decode_split_latent grid=65536",
-                                                             "decode_merge<true, 512> grid=131072"]),
+                       "roofline": decode_roofline(ssa_gbs, ["decode_split_latent ssa",
+                                                             "decode_merge<true, 512> ssa"]),
                        "timing": f"HIP graph of {reps * n_inst} calls rotating over {n_inst} instances"},
         "full_attn_decode": {"us": full_ms * 1e3, "bytes": full_bytes, "GB/s": full_gbs,
-                             "roofline": decode_roofline(full_gbs, ["decode_split_latent grid=524288",
-                                                                    "decode_merge<true, 512> grid=131072"])},
+                             "roofline": decode_roofline(full_gbs, ["decode_split_latent full",
+                                                                    "decode_merge<true, 512> full"])},
         "ssa_over_full_time": ssa_ms / full_ms,
     }
     del graph, insts, outs, base, ws_ssa, ws_full
@@ -671,7 +670,9 @@ def bench_decode_ragged(iters: int):
     nbytes = decode_bytes(cfg, inp.lens, sel, inputs.PAGE_SIZE)
     gbs = nbytes / (ms * 1e-3) / 1e9
     res = {"workload": cfg.name, "ssa_decode": {"us": ms * 1e3, "bytes": nbytes, "GB/s": gbs,
-                                                "roofline": decode_roofline(gbs)}}
+                                                "roofline": decode_roofline(
+                                                    gbs, ["decode_split_valu<true, 128, 1, false> ragged",
+                                                          "decode_merge<true, 128> ragged"])}}
     del inp, out, ws
     free_gpu()
     return res
@@ -718,6 +719,7 @@ def profile_run(what: str):
             step()
     elif what == "decode":
         bench_decode_latent(64)
+        bench_decode_ragged(8)
     elif what == "backward":
         _, step = backward_setup(inputs.PREFILL_BF16_32K)
         for _ in range(3):

@@ -42,6 +42,12 @@ constexpr int kThreads = 256;
 // rescaled; probabilities stay below 2^8, far from fp32/bf16 overflow.
 constexpr float kRescaleSlack = 8.f;
 
+// Compile-time tag: whether a sub-tile is known to need no mask.
+template <bool W>
+struct Whole {
+    static constexpr bool value = W;
+};
+
 // ---------------------------------------------------------------------------
 // bf16: pipelined direct-to-LDS kernel.
 // ---------------------------------------------------------------------------
@@ -307,11 +313,26 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     const int r_last = r_first + 31 < n_end - 1 ? r_first + 31 : n_end - 1;
     const int lo_first_w = local_start(geo, r_first), lo_last_w = local_start(geo, r_last);
 
-    auto compute = [&](int t, const uint16_t *kb, const uint16_t *vb) __attribute__((always_inline)) {
+    // Whether sub-tile t (of the sink or local range) is attended by every
+    // row of this wave at every key: then it needs no mask.
+    auto whole_at = [&](int t) __attribute__((always_inline)) -> bool {
+        const SubTile st = sub_tile<false>(tr, t);
+        const bool local = t >= tr.n_sink;
+        return r_first < n_end && st.j0 + kBN <= st.re && (!local || st.j0 >= lo_last_w) &&
+               st.j0 + kBN - 1 <= r_first;
+    };
+
+    // One sub-tile. With a true `whole` tag the caller knows the sub-tile
+    // needs no mask, and this copy has no mask code at all: a copy that
+    // chooses among the mask classes at run time keeps the scores of its
+    // paths in different registers and pays for moving them where the paths
+    // join.
+    auto compute = [&](auto whole, int t, const uint16_t *kb, const uint16_t *vb) __attribute__((always_inline)) {
         const SubTile st = sub_tile<DUAL>(tr, t);
-        bool no_mask, causal_only;
+        bool no_mask = true, causal_only = false;
         int edge = i;  // in a causal_only sub-tile, keys up to edge are attended
-        if (DUAL && t >= tr.n_total) {
+        if constexpr (decltype(whole)::value) {
+        } else if (DUAL && t >= tr.n_total) {
             // Complement sub-tile: key j (>= s*b) is attended iff j < lo_i,
             // which also keeps out the re-read rows past the range end.
             if (r_first >= n_end || st.j0 >= lo_last_w) return;
@@ -459,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         }
     };
     auto step = [&](int t, const uint16_t *kb, const uint16_t *vb) __attribute__((always_inline)) {
-        compute(t, kb, vb);
+        compute(Whole<false>{}, t, kb, vb);
         if constexpr (DUAL) {
             if (t == tr.n_total - 1) store_out(a.o, a.lse);  // the SSA result
         }
@@ -479,18 +500,38 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         }
         issue(0, k_buf0, v_buf0);
     }
-    for (; t + 2 < T; t += 2) {
-        issue(t + 1, k_buf1, v_buf1);
-        wait_vmcnt<NW>();
-        barrier_no_fence();
-        step(t, k_buf0, v_buf0);
-        barrier_lds_drained();
-        issue(t + 2, k_buf0, v_buf0);
-        wait_vmcnt<NW>();
-        barrier_no_fence();
-        step(t + 1, k_buf1, v_buf1);
-        barrier_lds_drained();
+    // The loop covers sub-tiles [0, n_loop). A wave whose rows attend all of
+    // them whole (every tile past the first l blocks when the block size is a
+    // multiple of 64) runs a copy without mask code; the other waves of the
+    // work-group may run the general copy, with the same transfers and
+    // barriers in the same order.
+    const int n_loop = 2 * ((T - 1) / 2);
+    bool whole_loop = false;
+    if constexpr (!DUAL) {
+        if (n_loop > 0) {
+            const int ts = imin(tr.n_sink, n_loop) - 1;  // last sink sub-tile in the loop
+            whole_loop = (ts < 0 || whole_at(ts)) &&
+                         (tr.n_sink >= n_loop || (whole_at(tr.n_sink) && whole_at(n_loop - 1)));
+        }
     }
+    auto loop = [&](auto whole) __attribute__((always_inline)) {
+        for (; t + 2 < T; t += 2) {
+            issue(t + 1, k_buf1, v_buf1);
+            wait_vmcnt<NW>();
+            barrier_no_fence();
+            if constexpr (decltype(whole)::value) compute(whole, t, k_buf0, v_buf0);
+            else step(t, k_buf0, v_buf0);
+            barrier_lds_drained();
+            issue(t + 2, k_buf0, v_buf0);
+            wait_vmcnt<NW>();
+            barrier_no_fence();
+            if constexpr (decltype(whole)::value) compute(whole, t + 1, k_buf1, v_buf1);
+            else step(t + 1, k_buf1, v_buf1);
+            barrier_lds_drained();
+        }
+    };
+    if (whole_loop) loop(Whole<true>{});
+    else loop(Whole<false>{});
     if (t + 1 < T) {
         issue(t + 1, k_buf1, v_buf1);
         wait_vmcnt<NW>();
