@@ -313,10 +313,11 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     const int r_last = r_first + 31 < n_end - 1 ? r_first + 31 : n_end - 1;
     const int lo_first_w = local_start(geo, r_first), lo_last_w = local_start(geo, r_last);
 
-    // Whether sub-tile t (of the sink or local range) is attended by every
-    // row of this wave at every key: then it needs no mask.
+    // Whether sub-tile t is attended by every row of this wave at every key:
+    // then it needs no mask.
     auto whole_at = [&](int t) __attribute__((always_inline)) -> bool {
-        const SubTile st = sub_tile<false>(tr, t);
+        const SubTile st = sub_tile<DUAL>(tr, t);
+        if (DUAL && t >= tr.n_total) return r_first < n_end && st.j0 + kBN <= lo_first_w;
         const bool local = t >= tr.n_sink;
         return r_first < n_end && st.j0 + kBN <= st.re && (!local || st.j0 >= lo_last_w) &&
                st.j0 + kBN - 1 <= r_first;
@@ -479,10 +480,11 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             lse_out[li] = (m_run + log2f(l_tot)) * kLn2;
         }
     };
-    auto step = [&](int t, const uint16_t *kb, const uint16_t *vb) __attribute__((always_inline)) {
-        compute(Whole<false>{}, t, kb, vb);
-        if constexpr (DUAL) {
-            if (t == tr.n_total - 1) store_out(a.o, a.lse);  // the SSA result
+    auto step = [&](auto whole, int t, const uint16_t *kb, const uint16_t *vb) __attribute__((always_inline)) {
+        compute(whole, t, kb, vb);
+        // The SSA result. Copies without masks run past the SSA range only.
+        if constexpr (DUAL && !decltype(whole)::value) {
+            if (t == tr.n_total - 1) store_out(a.o, a.lse);
         }
     };
 
@@ -504,46 +506,57 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     // them whole (every tile past the first l blocks when the block size is a
     // multiple of 64) runs a copy without mask code; the other waves of the
     // work-group may run the general copy, with the same transfers and
-    // barriers in the same order.
+    // barriers in the same order. In dual mode the diagonal sub-tiles sit
+    // between the local and the complement range: the SSA range runs the
+    // general copy, and the complement range, whole for every row when the
+    // tile's rows share one window start, chooses its copy by itself.
     const int n_loop = 2 * ((T - 1) / 2);
-    bool whole_loop = false;
-    if constexpr (!DUAL) {
-        if (n_loop > 0) {
-            const int ts = imin(tr.n_sink, n_loop) - 1;  // last sink sub-tile in the loop
-            whole_loop = (ts < 0 || whole_at(ts)) &&
-                         (tr.n_sink >= n_loop || (whole_at(tr.n_sink) && whole_at(n_loop - 1)));
-        }
-    }
-    auto loop = [&](auto whole) __attribute__((always_inline)) {
-        for (; t + 2 < T; t += 2) {
-            issue(t + 1, k_buf1, v_buf1);
-            wait_vmcnt<NW>();
-            barrier_no_fence();
-            if constexpr (decltype(whole)::value) compute(whole, t, k_buf0, v_buf0);
-            else step(t, k_buf0, v_buf0);
-            barrier_lds_drained();
-            issue(t + 2, k_buf0, v_buf0);
-            wait_vmcnt<NW>();
-            barrier_no_fence();
-            if constexpr (decltype(whole)::value) compute(whole, t + 1, k_buf1, v_buf1);
-            else step(t + 1, k_buf1, v_buf1);
-            barrier_lds_drained();
-        }
+    auto pair = [&](auto whole) __attribute__((always_inline)) {
+        issue(t + 1, k_buf1, v_buf1);
+        wait_vmcnt<NW>();
+        barrier_no_fence();
+        step(whole, t, k_buf0, v_buf0);
+        barrier_lds_drained();
+        issue(t + 2, k_buf0, v_buf0);
+        wait_vmcnt<NW>();
+        barrier_no_fence();
+        step(whole, t + 1, k_buf1, v_buf1);
+        barrier_lds_drained();
     };
-    if (whole_loop) loop(Whole<true>{});
-    else loop(Whole<false>{});
+    int t_whole = 0;  // first sub-tile of the range checked for the copy without masks
+    if constexpr (DUAL) {
+        for (; t + 2 < T && t < tr.n_total; t += 2) pair(Whole<false>{});
+        t_whole = t;
+    }
+    // The dual kernel with d_qk = 192 has no registers for a second copy.
+    constexpr bool kWholeCopy = !(DUAL && DQK > 128);
+    bool whole_loop = false;
+    if (kWholeCopy && t < n_loop) {
+        // Whole-ness is monotone over each range (the window start bounds a
+        // local or complement sub-tile from one side, the rows from the
+        // other), so the ends of each range decide it.
+        const int ts = imin(tr.n_sink, n_loop) - 1;  // last sink sub-tile in the loop
+        if (DUAL && t_whole >= tr.n_total) whole_loop = whole_at(t_whole) && whole_at(n_loop - 1);
+        else whole_loop = (ts < 0 || whole_at(ts)) &&
+                          (tr.n_sink >= n_loop || (whole_at(tr.n_sink) && whole_at(n_loop - 1)));
+    }
+    if (kWholeCopy && whole_loop) {
+        for (; t + 2 < T; t += 2) pair(Whole<kWholeCopy>{});
+    } else {
+        for (; t + 2 < T; t += 2) pair(Whole<false>{});
+    }
     if (t + 1 < T) {
         issue(t + 1, k_buf1, v_buf1);
         wait_vmcnt<NW>();
         barrier_no_fence();
-        step(t, k_buf0, v_buf0);
+        step(Whole<false>{}, t, k_buf0, v_buf0);
         wait_vmcnt<0>();
         barrier_no_fence();
-        step(t + 1, k_buf1, v_buf1);
+        step(Whole<false>{}, t + 1, k_buf1, v_buf1);
     } else if (t < T) {
         wait_vmcnt<0>();
         barrier_no_fence();
-        step(t, k_buf0, v_buf0);
+        step(Whole<false>{}, t, k_buf0, v_buf0);
     }
 
     // Epilogue: O = O / l, lse = ln 2 * (m + log2 l).
