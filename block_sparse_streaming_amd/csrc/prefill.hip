@@ -147,7 +147,20 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
 
     // Q^T operand, resident in registers for the whole tile.
     bf16x8 qf[NQ];
-    {
+
+    // The K / V transfers. For d_qk <= 128 they are issued untracked: the
+    // compiler's own tracking of these LDS writes does not survive the loop
+    // and adds a full wait before one of the two buffers' P.V reads, stalling
+    // on the transfer just issued for the next sub-tile; the explicit waits
+    // and barriers below order both buffers. d_qk = 192 (ten transfers per
+    // wave and stage) keeps the tracked form, whose loop has no such wait
+    // and no M0 save / restore per transfer.
+    constexpr bool kTrackedDma = DQK > 128;
+    auto dma = [&](const void *src, uint16_t *dst) __attribute__((always_inline)) {
+        if constexpr (kTrackedDma) dma16(src, dst);
+        else dma16_untracked(src, lds_addr(dst));
+    };
+    auto load_q = [&]() __attribute__((always_inline)) {
         const uint16_t *qrow = qbase + row_idx * a.qs[1] + 8 * hi;
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks) {
@@ -155,7 +168,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             if (row_ok) w = *(const u32x4 *)(qrow + ks * 16);
             qf[ks] = __builtin_bit_cast(bf16x8, w);
         }
-    }
+    };
+    if constexpr (kTrackedDma) load_q();
 
     // Direct transfers: lane slot p of transfer n covers tile row p / C at
     // physical unit p % C, which holds logical unit (p % C) ^ swz(row). Byte
@@ -231,9 +245,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             const char *kt = (const char *)(kbase + pg0 * a.ks[0] + (int64_t)sl0 * a.ks[1]);
             const char *vt = (const char *)(vbase + pg0 * a.vs[0] + (int64_t)sl0 * a.vs[1]);
 #pragma unroll
-            for (int n = 0; n < NIK; ++n) dma16(kt + koff[n], kb + (wave * NIK + n) * 512);
+            for (int n = 0; n < NIK; ++n) dma(kt + koff[n], kb + (wave * NIK + n) * 512);
 #pragma unroll
-            for (int n = 0; n < NIV; ++n) dma16(vt + voff[n], vb + (wave * NIV + n) * 512);
+            for (int n = 0; n < NIV; ++n) dma(vt + voff[n], vb + (wave * NIV + n) * 512);
             return;
         }
         auto src = [&](int p, int C, int swz, int64_t s0, int64_t s1) __attribute__((always_inline)) {
@@ -244,12 +258,12 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
 #pragma unroll
         for (int n = 0; n < NIK; ++n) {
             const int p = (wave * NIK + n) * 64 + lane;
-            dma16(kbase + src(p, CK, k_swz<CK>(p / CK), a.ks[0], a.ks[1]), kb + (wave * NIK + n) * 512);
+            dma(kbase + src(p, CK, k_swz<CK>(p / CK), a.ks[0], a.ks[1]), kb + (wave * NIK + n) * 512);
         }
 #pragma unroll
         for (int n = 0; n < NIV; ++n) {
             const int p = (wave * NIV + n) * 64 + lane;
-            dma16(vbase + src(p, CV, v_swz<CV>(p / CV), a.vs[0], a.vs[1]), vb + (wave * NIV + n) * 512);
+            dma(vbase + src(p, CV, v_swz<CV>(p / CV), a.vs[0], a.vs[1]), vb + (wave * NIV + n) * 512);
         }
     };
     auto issue = [&](int t, uint16_t *kb, uint16_t *vb) __attribute__((always_inline)) {
@@ -263,19 +277,19 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         const char *vt = (const char *)(vbase + (int64_t)st.j0 * a.vs[1]);
         if (kKeepOffsets && rows_valid >= kBN) {
 #pragma unroll
-            for (int n = 0; n < NIK; ++n) dma16(kt + koff[n], kb + (wave * NIK + n) * 512);
+            for (int n = 0; n < NIK; ++n) dma(kt + koff[n], kb + (wave * NIK + n) * 512);
 #pragma unroll
-            for (int n = 0; n < NIV; ++n) dma16(vt + voff[n], vb + (wave * NIV + n) * 512);
+            for (int n = 0; n < NIV; ++n) dma(vt + voff[n], vb + (wave * NIV + n) * 512);
         } else {
 #pragma unroll
             for (int n = 0; n < NIK; ++n) {
                 const int p = (wave * NIK + n) * 64 + lane;
-                dma16(kt + dma_off(p, CK, k_swz<CK>(p / CK), ks1, rows_valid), kb + (wave * NIK + n) * 512);
+                dma(kt + dma_off(p, CK, k_swz<CK>(p / CK), ks1, rows_valid), kb + (wave * NIK + n) * 512);
             }
 #pragma unroll
             for (int n = 0; n < NIV; ++n) {
                 const int p = (wave * NIV + n) * 64 + lane;
-                dma16(vt + dma_off(p, CV, v_swz<CV>(p / CV), vs1, rows_valid), vb + (wave * NIV + n) * 512);
+                dma(vt + dma_off(p, CV, v_swz<CV>(p / CV), vs1, rows_valid), vb + (wave * NIV + n) * 512);
             }
         }
     };
@@ -501,6 +515,15 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             wait_vmcnt<0>();
         }
         issue(0, k_buf0, v_buf0);
+    }
+    if constexpr (!kTrackedDma) {
+        // q after the first sub-tile's transfers, and one wait for both
+        // (each is needed before the first product). The compiler does not
+        // see the untracked transfers; without this wait it would order the
+        // q loads by a full wait inside the loop, which would also wait for
+        // the next sub-tile's transfers.
+        load_q();
+        wait_vmcnt<0>();
     }
     // The loop covers sub-tiles [0, n_loop). A wave whose rows attend all of
     // them whole (every tile past the first l blocks when the block size is a
