@@ -75,6 +75,8 @@ SMALL = [
     (1, 1300, 2, 2, 128, 128, (300, 1, 2), 0.7),      # sink spans several key tiles
     (1, 700, 8, 2, 64, 64, (32, 2, 3), 0.5),          # GQA group 4
     (1, 900, 2, 2, 192, 128, (128, 12, 1), 0.5),      # every key is a sink key
+    (1, 3000, 2, 2, 128, 128, (64, 1, 16), 0.5),      # waves of one tile take different loop copies
+    (1, 3000, 2, 1, 64, 64, (192, 1, 5), 0.5),        # window starts inside a tile
 ]
 
 

@@ -61,6 +61,11 @@ SMALL = [
     (torch.bfloat16, 1, 1300, 2, 2, 128, 128, (128, 0, 1)),     # no sink, own block only
     (torch.bfloat16, 1, 1300, 2, 2, 128, 128, (7, 5, 1)),
     (torch.bfloat16, 1, 1300, 2, 2, 128, 128, (128, 1, 64)),    # window longer than N
+    # 64-key blocks, long window: in every late tile the two waves of the
+    # upper rows take the loop copy without masks, the two lower ones the
+    # general copy (their window starts one block later)
+    (torch.bfloat16, 1, 3000, 2, 2, 128, 128, (64, 1, 16)),
+    (torch.bfloat16, 1, 3000, 2, 1, 64, 64, (192, 1, 5)),       # window starts inside a tile
     (torch.float32, 1, 1300, 2, 2, 128, 128, (128, 1, 7)),
     (torch.float32, 2, 700, 4, 2, 64, 64, (32, 2, 3)),
 ]
