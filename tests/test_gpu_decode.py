@@ -113,7 +113,7 @@ def test_latent_tiny_pages_wide_table(page_size):
     _check(cfg, inp, PAT, full=True, what=f"latent P{page_size} full", page_size=page_size)
 
 
-def test_config3_latent_full_size():
+def test_latent_128k_full_size():
     """32 sequences x 131072 tokens, shuffled pages: SSA decode on every
     sequence, full decode on two of them (the oracle's cost is the limit)."""
     cfg = inputs.DECODE_LATENT_128K
@@ -127,7 +127,7 @@ def test_config3_latent_full_size():
     _check(cfg, part, PAT, full=True, what=cfg.name + " full (2 seqs)")
 
 
-def test_config5_ragged_full_size():
+def test_ragged_full_size():
     cfg = inputs.DECODE_RAGGED
     inp = inputs.decode_inputs(cfg, DEV)
     assert min(inp.lens) < 1024

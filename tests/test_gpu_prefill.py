@@ -39,7 +39,7 @@ def _run_and_check(q, k, v, pattern, scale, rows=None, what=""):
     return o
 
 
-def test_config1_fp32_full():
+def test_fp32_2k_full():
     cfg = inputs.PREFILL_FP32_2K
     q, k, v = inputs.prefill_inputs(cfg, DEV)
     _run_and_check(q, k, v, inputs.PATTERN, cfg.scale, what=cfg.name)
@@ -107,7 +107,7 @@ def _sample_tiles(num_tiles, fixed, n_random, seed):
     return sorted(set(fixed) | set(int(x) for x in extra))
 
 
-def test_config2_sampled_tiles():
+def test_bf16_32k_sampled_tiles():
     cfg = inputs.PREFILL_BF16_32K
     q, k, v = inputs.prefill_inputs(cfg, DEV)
     tiles = _sample_tiles(cfg.N // 128, [0, 1, 6, 7, 8, 9, 128, 255], 6, 2)
@@ -115,7 +115,7 @@ def test_config2_sampled_tiles():
     _run_and_check(q, k, v, inputs.PATTERN, cfg.scale, rows=rows, what=cfg.name)
 
 
-def test_config4_stratified_sample():
+def test_bf16_256k_stratified_sample():
     """Every head; query blocks 0..8, 1023, 1024, 2047 and 8 seeded random blocks."""
     cfg = inputs.PREFILL_BF16_256K
     q, k, v = inputs.prefill_inputs(cfg, DEV)
