@@ -637,19 +637,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
     const int row = blockIdx.x * (kMergeThreads / 64) + (threadIdx.x >> 6);  // bb * Hq + h
     if (row >= a.B * a.Hq) return;
     const int bb = row / a.Hq;
-    const int64_t L = row_context(a, bb);
     Elem *out = (Elem *)a.o + (int64_t)row * D + E * lane;
-    int ns = 0;
-    if (L > 0) {
-        const Sel sel = select_tokens(L, a);
-        ns = (int)((sel.total + a.plan.split_tokens - 1) / a.plan.split_tokens) + list_splits(a);
-    }
-    if (ns == 0) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) out[e] = Elem(0);
-        if (lane == 0 && a.lse) a.lse[row] = -INFINITY;
-        return;
-    }
     const int64_t slot0 = (int64_t)row * a.plan.max_splits;
     const float *wl = a.ws_lse + slot0;
     // The latent split kernel (the only one with D = 512) stores its partial
@@ -658,7 +646,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
     using Part = std::conditional_t<kPartBF16, uint16_t, float>;
     const Part *wo = (const Part *)a.ws_o + slot0 * D + E * lane;
 
-    // Partial rows of splits s0 .. s0+7 (clamped to the last split).
+    // Partial rows of splits s0 .. s0+7 (clamped to nb - 1).
     float part[kMergeBatch][E];
     auto load_batch = [&](int s0, int nb) __attribute__((always_inline)) {
 #pragma unroll
@@ -686,14 +674,33 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
             }
         }
     };
-    // The first batch is requested before the weights are known.
-    load_batch(0, ns < 64 ? ns : 64);
-    float M = -INFINITY;
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, wl[s]);
+    // The first batch of partial rows and the lse of the first 64 splits are
+    // requested before the row's split count is known (it needs the context
+    // length): the slots exist for every row. Slots past the count hold
+    // stale values; they are never used (selects and uniform branches below,
+    // not products with a zero weight).
+    const int nb0 = a.plan.max_splits < 64 ? a.plan.max_splits : 64;
+    load_batch(0, nb0);
+    const float lse0 = lane < nb0 ? wl[lane] : -INFINITY;
+
+    const int64_t L = row_context(a, bb);
+    int ns = 0;
+    if (L > 0) {
+        const Sel sel = select_tokens(L, a);
+        ns = (int)((sel.total + a.plan.split_tokens - 1) / a.plan.split_tokens) + list_splits(a);
+    }
+    if (ns == 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) out[e] = Elem(0);
+        if (lane == 0 && a.lse) a.lse[row] = -INFINITY;
+        return;
+    }
+    float M = lane < ns ? lse0 : -INFINITY;
+    for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, wl[s]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float Z = 0.f;
-    for (int s = lane; s < ns; s += 64) Z += fast_exp2(wl[s] - M);
+    float Z = lane < ns ? fast_exp2(lse0 - M) : 0.f;
+    for (int s = lane + 64; s < ns; s += 64) Z += fast_exp2(wl[s] - M);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) Z += __shfl_xor(Z, o);
     const float inv = 1.f / Z;
@@ -702,17 +709,19 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
     for (int s64 = 0; s64 < ns; s64 += 64) {
-        const float wlane = s64 + lane < ns ? fast_exp2(wl[s64 + lane] - M) * inv : 0.f;
+        const float lw = s64 == 0 ? lse0 : (s64 + lane < ns ? wl[s64 + lane] : -INFINITY);
+        const float wlane = s64 + lane < ns ? fast_exp2(lw - M) * inv : 0.f;
         const int nb = ns - s64 < 64 ? ns - s64 : 64;
         if (s64 > 0) load_batch(0, nb);
         for (int s0 = 0; s0 < nb; s0 += kMergeBatch) {
             if (s0 > 0) load_batch(s0, nb);
 #pragma unroll
             for (int u = 0; u < kMergeBatch; ++u) {
-                const float wf =
-                    s0 + u < nb ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlane), s0 + u)) : 0.f;
+                if (s0 + u < nb) {  // uniform
+                    const float wf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlane), s0 + u));
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(wf, part[u][e], acc[e]);
+                    for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(wf, part[u][e], acc[e]);
+                }
             }
         }
         wo += (int64_t)64 * D;
