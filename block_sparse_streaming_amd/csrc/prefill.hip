@@ -21,7 +21,11 @@
 //    registers are spent on staging. Rows are XOR-swizzled in 16-byte units so
 //    that both the score-operand reads (16 keys, one column) and the transpose
 //    reads (4 keys x 64 bytes) hit distinct LDS banks.
-//  * Only sub-tiles that cross a window edge or the diagonal are masked.
+//  * Only sub-tiles that cross a window edge or the diagonal are masked. A
+//    wave whose rows attend every sub-tile of the steady-state loop whole runs
+//    a second copy of the loop with no mask code (chosen once per loop: a
+//    per-sub-tile choice leaves the paths' registers apart and costs moves
+//    where they join).
 //  * Work-group ids are remapped so that each XCD (own L2) runs a contiguous
 //    run of query tiles of one head: the sink tile and overlapping local tiles
 //    are then L2 hits.
@@ -503,10 +507,11 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     };
 
     // Two-stage pipeline: sub-tile t+1 streams into the other buffer while t
-    // is computed. Buffers are separate LDS objects so the compiler can tell
-    // the in-flight transfers from the buffer being read; the steady-state loop
-    // issues and waits unconditionally and the last one or two sub-tiles are
-    // peeled, so every wait is a fixed count.
+    // is computed. Buffers are separate LDS objects so that, for the tracked
+    // transfers of d_qk = 192, the compiler can tell the in-flight transfers
+    // from the buffer being read; the steady-state loop issues and waits
+    // unconditionally and the last one or two sub-tiles are peeled, so every
+    // wait is a fixed count.
     const int T = DUAL ? tr.n_all : tr.n_total;
     int t = 0;
     if (T > 0) {
