@@ -46,9 +46,10 @@ struct Sel {
 // Context length (query position + 1) and page-table row of query row r.
 // Row-map entries are clamped to the table (a row the map left unwritten,
 // of a chunk longer than max_q_len, reads only valid pages).
+// Context length of query row r, clamped to the page table's capacity so that
+// no length reads past its table row.
 __device__ __forceinline__ int64_t row_context(const DecodeArgs &a, int r) {
-    if (!a.row_ctx) return a.ctx_lens[r];
-    const int64_t L = a.row_ctx[r], cap = (int64_t)a.max_pages * a.page_size;
+    const int64_t L = a.row_ctx ? a.row_ctx[r] : a.ctx_lens[r], cap = (int64_t)a.max_pages * a.page_size;
     return L < cap ? L : cap;
 }
 __device__ __forceinline__ int64_t row_sequence(const DecodeArgs &a, int r) {

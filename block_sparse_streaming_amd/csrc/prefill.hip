@@ -127,7 +127,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         q_start = a.cu_q[bb];
         const int q_len = a.cu_q[bb + 1] - q_start;
         if (qt * kBM >= q_len) return;  // this sequence has fewer tiles (uniform)
-        geo.N = a.ctx_lens[bb];
+        const int64_t cap = (int64_t)a.max_pages * a.page_size;  // no length reads past the table row
+        geo.N = a.ctx_lens[bb] < cap ? a.ctx_lens[bb] : (int)cap;
         pos0 = geo.N - q_len;
         pos0 = pos0 > 0 ? pos0 : 0;     // q_len <= ctx is a precondition; stay in bounds
         q0 = pos0 + qt * kBM;

@@ -203,3 +203,42 @@ def test_decode_matches_last_prefill_row():
                          torch.tensor([L], dtype=torch.int32, device=DEV), **PAT)
         diff = (o_d.float() - o_p[:, L - 1].float()).abs().max().item()
         assert diff <= 2e-2, (L, diff)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("latent", [False, True])
+def test_context_length_clamped_to_table_row(latent):
+    """A context length past the page table's capacity (max_pages x
+    page_size) attends as the capacity: bit-identical to the call at exactly
+    the capacity, and the other sequence is unaffected. (Were the length not
+    clamped, sequence 0 would read sequence 1's table row, still inside the
+    table.)"""
+    page, max_pages = 16, 8
+    cap = page * max_pages
+    g = torch.Generator(device=DEV).manual_seed(91)
+    if latent:
+        Hq, Hkv, dqk, dv = 16, 1, 576, 512
+    else:
+        Hq, Hkv, dqk, dv = 4, 2, 128, 128
+    n_pages = 2 * max_pages
+    kc = torch.randn(n_pages, page, Hkv, dqk, device=DEV, generator=g).bfloat16()
+    vc = kc if latent else torch.randn(n_pages, page, Hkv, dv, device=DEV, generator=g).bfloat16()
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(92)).to(torch.int32)
+    table = perm.view(2, max_pages).to(DEV)
+    q = torch.randn(2, Hq, dqk, device=DEV, generator=g).bfloat16()
+    say("decode clamp", "latent" if latent else "mha", cap)
+    for full in (False, True):
+        call = ssa.full_decode if full else ssa.decode
+        kw = {} if full else dict(block=16, sink=1, local=3)
+        if latent:
+            kw["scale"] = 1.0 / math.sqrt(dqk)
+            vv = kc[..., :dv]
+        else:
+            vv = vc
+        ref, ref_lse = call(q, kc, vv, table, torch.tensor([cap, 100], dtype=torch.int32, device=DEV),
+                            return_lse=True, **kw)
+        got, got_lse = call(q, kc, vv, table, torch.tensor([cap + 37, 100], dtype=torch.int32, device=DEV),
+                            return_lse=True, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), ("full" if full else "ssa")
+        assert torch.equal(got_lse, ref_lse), ("full" if full else "ssa")
