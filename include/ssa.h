@@ -38,7 +38,9 @@
  *    row must start on a 16-byte boundary (pointers and strides aligned).
  *  - Accumulation is fp32. bf16 outputs are rounded to nearest-even.
  *  - Device-resident integers (page ids, context lengths) are trusted: they
- *    are not range-checked on the host.
+ *    are not range-checked on the host. A context length above the page
+ *    table's capacity (max_pages x page_size) is taken as that capacity; a
+ *    page id outside the cache is not detected.
  */
 #ifndef BLOCK_SPARSE_STREAMING_SSA_H
 #define BLOCK_SPARSE_STREAMING_SSA_H
