@@ -125,7 +125,8 @@ def test_chunked_prefill_shapes(dqk, dv, Hq, Hkv):
 @pytest.mark.parametrize("pattern", [dict(block=128, sink=0, local=1), dict(block=64, sink=2, local=3),
                                      dict(block=16, sink=1, local=4), dict(block=100, sink=1, local=2),
                                      dict(block=50, sink=3, local=5), dict(block=300, sink=1, local=2),
-                                     dict(block=7, sink=5, local=1), dict(block=128, sink=1, local=64)],
+                                     dict(block=7, sink=5, local=1), dict(block=128, sink=1, local=64),
+                                     dict(block=64, sink=1, local=16)],  # waves of a tile: both loop copies
                          ids=lambda p: f"b{p['block']}s{p['sink']}l{p['local']}")
 def test_chunked_prefill_patterns(pattern):
     _run(_inp((1300, 2500, 777), (400, 1000, 777), 2, 2, 128, 128, seed=750), pattern, 128 ** -0.5,
