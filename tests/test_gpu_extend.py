@@ -172,6 +172,17 @@ def test_chunked_prefill_full_size_sampled():
     _run(inp, PAT, 128 ** -0.5, "chunk full size", rows=rows)
 
 
+def test_multi_token_decode_full_size_sampled():
+    """The multi-token decode workload the benchmark times: 32 sequences at
+    131,072 tokens, four new rows each, on the latent shape (64 query heads on
+    one 576-wide latent head), shuffled 128-token pages. Every row is computed;
+    the rows of eight sequences are checked against the oracle."""
+    B, T = 32, inputs.EXTEND_MTP_Q
+    inp = _inp((inputs.EXTEND_MTP_LEN,) * B, (T,) * B, 64, 1, 576, 512, seed=inputs.EXTEND_MTP_SEED, latent=True)
+    rows = np.concatenate([np.arange(b * T, (b + 1) * T) for b in (0, 3, 7, 12, 18, 23, 29, 31)])
+    _run(inp, PAT, 576 ** -0.5, "mtp full size", latent_dv=512, rows=rows)
+
+
 def test_rejects_small_workspace():
     """One-row chunks run on the decode kernels, which need the workspace."""
     inp = _inp((500, 600), (1, 1), 4, 4, 128, 128, seed=790)
