@@ -18,7 +18,8 @@ Inputs are synthetic (seeded N(0,1)) and resident in HBM before timing.
 Timing uses HIP events recorded on the stream the kernels are launched on
 (torch's current stream, which the binding passes to the library).
 
---profile {prefill,decode,backward,dual,extend,hybrid,copy} runs one short workload and prints nothing
+--profile {prefill,prefill_fp32,prefill_256k,decode,backward,backward_256k,dual,extend,hybrid,copy}
+runs one short workload and prints nothing
 else, for rocprofv3 counter collection (copy: a plain 1 GiB device copy whose
 counter readings calibrate FETCH_SIZE / WRITE_SIZE).
 """
@@ -713,9 +714,15 @@ def cpu_baseline():
 def profile_run(what: str):
     import torch
     from block_sparse_streaming_amd import inputs
-    if what == "prefill":
-        _, step = prefill_setup(inputs.PREFILL_BF16_32K)
+    if what in ("prefill", "prefill_fp32", "prefill_256k"):
+        cfg = {"prefill": inputs.PREFILL_BF16_32K, "prefill_fp32": inputs.PREFILL_FP32_2K,
+               "prefill_256k": inputs.PREFILL_BF16_256K}[what]
+        _, step = prefill_setup(cfg)
         for _ in range(3):
+            step()
+    elif what == "backward_256k":
+        _, step = backward_setup(inputs.PREFILL_BF16_256K)
+        for _ in range(2):
             step()
     elif what == "decode":
         bench_decode_latent(64)
@@ -749,7 +756,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--profile", choices=["prefill", "decode", "backward", "dual", "extend", "hybrid", "copy"], default=None)
+    ap.add_argument("--profile", choices=["prefill", "prefill_fp32", "prefill_256k", "decode", "backward",
+                                          "backward_256k", "dual", "extend", "hybrid", "copy"], default=None)
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the 32K prefill (and the CPU oracle)")
     args = ap.parse_args()
