@@ -139,6 +139,25 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     }
     const TileRanges tr = tile_ranges_at(geo, q0, q1);
     const int n_end = PAGED ? q1 : a.N;     // rows at positions >= n_end are not computed
+    // Visit order of the sub-tiles (plain mode, d_qk = 192): the full 128-key
+    // pairs of the local range before its last two sub-tiles are visited by
+    // absolute pair index modulo their count, so that the tiles running side
+    // by side on an XCD read the same key pairs at the same time (the softmax
+    // does not depend on the order). At 256K tokens x 64 heads this cuts the
+    // L2 misses 2.3x (their working set otherwise exceeds an XCD's L2); at
+    // d = 128 there are no re-reads to save and the order costs time. The
+    // sink range and the last two sub-tiles keep their place.
+    const int rot_n = (DQK > 128 && !DUAL && !PAGED) ? (tr.n_total - tr.n_sink - 2) >> 1 : 0;
+    const int rot_off = rot_n > 1 ? (tr.loc_begin >> 7) % rot_n : 0;
+    auto visit = [&](int t) __attribute__((always_inline)) -> int {
+        const int u = t - tr.n_sink;
+        if (rot_n > 1 && u >= 0 && u < 2 * rot_n) {
+            int p = (u >> 1) - rot_off;
+            p = p < 0 ? p + rot_n : p;
+            return tr.n_sink + 2 * p + (u & 1);
+        }
+        return t;
+    };
     const int i = tr.q0 + wave * 32 + l32;  // this lane's query row (its position)
     const bool row_ok = i < n_end;
     const int lo_i = local_start(geo, i);
@@ -276,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             issue_paged(t, kb, vb);
             return;
         }
-        const SubTile st = sub_tile<DUAL>(tr, t);
+        const SubTile st = sub_tile<DUAL>(tr, visit(t));
         const int rows_valid = st.re - st.j0;
         const char *kt = (const char *)(kbase + (int64_t)st.j0 * a.ks[1]);
         const char *vt = (const char *)(vbase + (int64_t)st.j0 * a.vs[1]);
@@ -348,7 +367,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     // paths in different registers and pays for moving them where the paths
     // join.
     auto compute = [&](auto whole, int t, const uint16_t *kb, const uint16_t *vb) __attribute__((always_inline)) {
-        const SubTile st = sub_tile<DUAL>(tr, t);
+        const SubTile st = sub_tile<DUAL>(tr, visit(t));
         bool no_mask = true, causal_only = false;
         int edge = i;  // in a causal_only sub-tile, keys up to edge are attended
         if constexpr (decltype(whole)::value) {
