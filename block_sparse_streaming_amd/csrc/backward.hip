@@ -166,6 +166,22 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
     const int i = tr.q0 + wave * 32 + l32;  // this lane's query row
     const bool row_ok = i < a.N;
     const int lo_i = local_start(a, i);
+    // Visit order at d_qk = 192, as in the forward: the full 128-key pairs of
+    // the local range (all but its last two sub-tiles) by absolute pair index
+    // modulo their count, so that tiles running side by side on an XCD read
+    // the same keys at the same time (their working set otherwise exceeds an
+    // XCD's L2 at 256K x 64 heads). dq does not depend on the order.
+    const int rot_n = DQK > 128 ? (tr.n_total - tr.n_sink - 2) >> 1 : 0;
+    const int rot_off = rot_n > 1 ? (tr.loc_begin >> 7) % rot_n : 0;
+    auto visit = [&](int t) -> int {
+        const int u = t - tr.n_sink;
+        if (rot_n > 1 && u >= 0 && u < 2 * rot_n) {
+            int p = (u >> 1) - rot_off;
+            p = p < 0 ? p + rot_n : p;
+            return tr.n_sink + 2 * p + (u & 1);
+        }
+        return t;
+    };
 
     // q and dO of row i as B operands (lane half hi holds 8 of each 16
     // columns), lse in log2 units, and D = dO . O over the whole row.
@@ -218,7 +234,7 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
 
     const uint32_t k_lds0 = lds_addr(&k_lds[0][0]), v_lds0 = lds_addr(&v_lds[0][0]);
     auto issue = [&](int t) {
-        const SubTile st = sub_tile(tr, t);
+        const SubTile st = sub_tile(tr, visit(t));
         const int rows_valid = st.re - st.j0;
         const char *kt = (const char *)(kbase + (int64_t)st.j0 * a.ks[1]);
         const char *vt = (const char *)(vbase + (int64_t)st.j0 * a.vs[1]);
@@ -266,7 +282,7 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
 
     auto compute = [&](auto buf, int t) {
         constexpr int BUF = decltype(buf)::value;
-        const SubTile st = sub_tile(tr, t);
+        const SubTile st = sub_tile(tr, visit(t));
         const bool local = t >= tr.n_sink;
         const int kend = st.j0 + kBN < st.re ? st.j0 + kBN : st.re;
         if (r_first >= a.N || st.j0 > r_last || (local && kend <= lo_first_w)) return;
