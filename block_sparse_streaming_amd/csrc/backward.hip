@@ -481,6 +481,18 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
     }
     const int nsub = r1 > r0 ? (r1 - r0 + KR - 1) / KR : 0;
     const int T = a.group * nsub;
+    // Visit order at d_qk = 192 (key tiles past the sink): the query
+    // sub-tiles by absolute index modulo their count, so that the key tiles
+    // an XCD runs side by side, whose row ranges are offset by two sub-tiles
+    // each, read the same sub-tiles at the same time instead of ~128
+    // different ones (more than an XCD's L2 at 256K x 64 heads). dk and dv
+    // do not depend on the order.
+    const int rot = (DQK > 128 && !part && nsub > 1) ? (r0 / KR) % nsub : 0;
+    auto row0 = [&](int t) -> int {
+        int u = t % nsub - rot;
+        u = u < 0 ? u + nsub : u;
+        return r0 + KR * u;
+    };
 
     // This lane's key: its K and V rows as B operands, and the rows that
     // attend it within this work-group's range: [j, up_j).
@@ -539,7 +551,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
         const uint32_t db = __builtin_amdgcn_readfirstlane(d_lds0 + slot * DBUF);
         const uint32_t sbuf = s_lds0 + slot * (NG * 512u);
         const int hh = g * a.group + t / nsub;
-        const int i0 = r0 + KR * (t % nsub);
+        const int i0 = row0(t);
         const int rows_valid = r1 - i0 < KR ? r1 - i0 : KR;
         const char *qt = (const char *)((const uint16_t *)a.q + bb * a.qs[0] + (int64_t)i0 * qs1 + hh * a.qs[2]);
         const char *dt = (const char *)((const uint16_t *)a.dout + bb * a.dos[0] + (int64_t)i0 * ds1 + hh * a.dos[2]);
@@ -604,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
         const char *qc = (const char *)q_lds[BUF];
         const char *dc = (const char *)d_lds[BUF];
         const float *sbf = s_lds[BUF];
-        const int i0 = r0 + KR * (t % nsub);
+        const int i0 = row0(t);
 #pragma unroll
         for (int qblk = 0; qblk < KR / 32; ++qblk) {
             const int ib = i0 + 32 * qblk;  // first row of the block
