@@ -71,6 +71,8 @@ SMALL = [
     (1, 1300, 2, 2, 128, 128, (128, 1, 64)),     # window longer than N
     (1, 700, 8, 2, 64, 64, (32, 2, 3)),          # GQA group 4
     (1, 900, 2, 2, 192, 128, (128, 12, 1)),      # every key is a sink key
+    (1, 1700, 2, 2, 192, 128, (64, 1, 16)),      # d_qk = 192, long window of small blocks
+    (1, 1900, 2, 2, 192, 128, (100, 2, 5)),      # d_qk = 192, blocks not aligned to tiles
 ]
 
 
