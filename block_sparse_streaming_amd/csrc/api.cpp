@@ -15,8 +15,13 @@ using ssa::DecodePlan;
 using ssa::PrefillArgs;
 
 constexpr int64_t kInt32Max = std::numeric_limits<int32_t>::max();
-// Target number of work-groups for a full-attention decode (8 per CU on 256 CUs).
-constexpr int64_t kFullDecodeTargetWgs = 2048;
+// Target number of work-groups for a full-attention decode: two per CU on
+// 256 CUs, i.e. long splits (8,192 tokens per split for 32 sequences at
+// 128K). Each work-group pays a fixed set-up and partial write-out, and
+// fewer, longer splits also leave the merge fewer partials; measured on the
+// 128K latent workload, 512 beat 1,024 by 7% and 2,048 by 11-14%, and 256
+// was level with 512.
+constexpr int64_t kFullDecodeTargetWgs = 512;
 // Attended tokens per split for the windowed (SSA) decode.
 constexpr int64_t kSsaSplitTokens = 128;
 
