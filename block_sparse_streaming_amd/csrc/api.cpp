@@ -22,6 +22,10 @@ constexpr int64_t kInt32Max = std::numeric_limits<int32_t>::max();
 // 128K latent workload, 512 beat 1,024 by 7% and 2,048 by 11-14%, and 256
 // was level with 512.
 constexpr int64_t kFullDecodeTargetWgs = 512;
+// Upper bound of a full-attention split. Without it a call with many
+// (sequence, head) rows (>= 512) would give every row a single split, and one
+// work-group would walk a whole long context while the others sit idle.
+constexpr int64_t kFullDecodeMaxSplit = 8192;
 // Attended tokens per split for the windowed (SSA) decode.
 constexpr int64_t kSsaSplitTokens = 128;
 
@@ -75,6 +79,7 @@ bool make_plan(ssa_dtype dtype, int32_t batch, int32_t heads_q, int32_t heads_kv
         max_tokens = max_ctx;
         const int64_t wgs_per_split = (int64_t)batch * heads_kv * plan->head_chunks;
         split = (max_tokens * wgs_per_split + kFullDecodeTargetWgs - 1) / kFullDecodeTargetWgs;
+        split = split < kFullDecodeMaxSplit ? split : kFullDecodeMaxSplit;
         split = split < 256 ? 256 : split;
     } else {
         const int64_t window = ((int64_t)pat.sink + pat.local) * pat.block;

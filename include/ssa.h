@@ -192,6 +192,8 @@ size_t ssa_prefill_backward_workspace_size(ssa_dtype dtype, int32_t batch, int32
  *              with equal strides: then the value is the first d_v entries of
  *              the key row (a latent cache, as in absorbed MLA).
  *   page_table [batch, max_pages] int32 physical page ids, row-major.
+ *   max_pages  the page table's row length; it follows page_table, the array
+ *              it describes.
  *   ctx_lens   [batch] int32 context lengths L, the new token included: its
  *              key and value are already in the cache and the query sits at
  *              position L - 1. Token t of a sequence is in page
@@ -203,9 +205,10 @@ size_t ssa_prefill_backward_workspace_size(ssa_dtype dtype, int32_t batch, int32
  *   workspace  device scratch of at least ssa_decode_workspace_size(...)
  *              bytes (same shape arguments, full = 0); no initial contents
  *              are required. Calls sharing one workspace must not overlap.
- * Compiled: bf16 or fp32 with d_qk, d_v in {64, 128, 256} and
- * heads_q / heads_kv in {1, 2, 4, 8}; bf16 latent shape d_qk = 576,
- * d_v = 512 with heads_q / heads_kv a multiple of 16.
+ * Compiled: bf16 or fp32 with d_qk = d_v in {64, 128, 256} and
+ * heads_q / heads_kv in {1, 2, 4, 8}, except group 8 at d = 256
+ * (SSA_ERR_UNSUPPORTED); bf16 latent shape d_qk = 576, d_v = 512 with
+ * heads_q / heads_kv a multiple of 16.
  */
 ssa_status ssa_decode(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
                       const int64_t k_strides[3], const int64_t v_strides[3],
@@ -231,8 +234,11 @@ ssa_status full_attn_decode(ssa_dtype dtype, const void *q, const void *k_cache,
 /*
  * Workspace bytes for ssa_decode (full = 0; pattern used) or full_attn_decode
  * (full = 1; pattern ignored). Returns 0 for arguments the decode calls would
- * reject. The workspace holds one fp32 partial output and one log-sum-exp per
- * (sequence, query head, split of the attended tokens).
+ * reject. It takes the decode call's shape arguments (dtype, head counts and
+ * dims, page size and table width), since the split plan depends on all of
+ * them. The workspace holds one partial output (bf16 for the latent shape,
+ * fp32 otherwise) and one log-sum-exp per (sequence, query head, split of
+ * the attended tokens).
  */
 size_t ssa_decode_workspace_size(ssa_dtype dtype, int32_t batch, int32_t heads_q,
                                  int32_t heads_kv, int32_t d_qk, int32_t d_v,
@@ -312,8 +318,9 @@ size_t ssa_extend_workspace_size(ssa_dtype dtype, int32_t batch, int32_t total_q
  * The window and the listed tokens are cut into splits of one size; one
  * merge combines all of a row's splits. Compiled: every shape ssa_decode
  * compiles (bf16 or fp32 with d_qk = d_v in {64, 128, 256} and heads_q /
- * heads_kv in {1, 2, 4, 8}; the bf16 latent shape). The list is shared by a
- * sequence's query heads. topk_k must be >= 1.
+ * heads_kv in {1, 2, 4, 8}, except group 8 at d = 256; the bf16 latent
+ * shape). The list is shared by a sequence's query heads. topk_k must be
+ * >= 1.
  */
 ssa_status hybrid_decode(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
                          const int64_t k_strides[3], const int64_t v_strides[3],

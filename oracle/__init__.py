@@ -296,3 +296,47 @@ def backward(q, k, v, dout, *, block=128, sink=1, local=7, scale, full=False, ro
     if rc != 0:
         raise ValueError("oracle_ssa_backward rejected its arguments")
     return dq, dk, dv
+
+
+def backward_keys(q, k, v, dout, keys, *, block=128, sink=1, local=7, scale):
+    """dk and dv of the listed key positions, from every query row that
+    attends them, without evaluating dq: the exact gradient of the prefill
+    operator (softmax attention over the SSA window) restricted to those keys.
+
+    With ``P_ij = exp(scale q_i.k_j - lse_i)`` over the attended set,
+    ``D_i = dout_i . o_i`` (the forward output: ``sum_j P_ij dout_i.v_j``),
+    ``dS_ij = P_ij (dout_i.v_j - D_i)``: ``dk_j = scale sum_i dS_ij q_i`` and
+    ``dv_j = sum_i P_ij dout_i``, summed over the query heads of a kv head.
+    lse and o come from ``prefill`` (double); the rows of a key are the
+    ``i >= j`` whose window holds it (the block rule of ``prefill``).
+
+    Returns ``(dk, dv)``: [B, len(keys), Hkv, d_qk] and [B, len(keys), Hkv,
+    d_v] in float64.
+    """
+    keys = np.asarray(keys, dtype=np.int64)
+    B, N, Hq, d_qk = q.shape
+    Hkv, d_v = k.shape[2], v.shape[3]
+    group = Hq // Hkv
+    if keys.size and (keys.min() < 0 or keys.max() >= N):
+        raise ValueError("key positions must lie in [0, N)")
+    i0 = int(keys.min()) if keys.size else N
+    rows = np.arange(i0, N)
+    o, lse, _ = prefill(q, k, v, block=block, sink=sink, local=local, scale=scale, rows=rows)
+    i = rows[:, None]
+    j = keys[None, :]
+    mask = (j <= i) & ((j // block < sink) | (j // block > i // block - local))
+    dk = np.zeros((B, keys.size, Hkv, d_qk))
+    dv = np.zeros((B, keys.size, Hkv, d_v))
+    for b in range(B):
+        for g in range(Hkv):
+            kj = _bf16_or_f32_to_f64(k[b, keys, g])                 # [K, d_qk]
+            vj = _bf16_or_f32_to_f64(v[b, keys, g])                 # [K, d_v]
+            for h in range(g * group, (g + 1) * group):
+                qi = _bf16_or_f32_to_f64(q[b, rows, h])             # [R, d_qk]
+                doi = _bf16_or_f32_to_f64(dout[b, rows, h])         # [R, d_v]
+                p = np.where(mask, np.exp(scale * (qi @ kj.T) - lse[b, h][:, None]), 0.0)
+                dd = np.einsum("rd,rd->r", doi, o[b, :, h])
+                ds = p * (doi @ vj.T - dd[:, None])
+                dk[b, :, g] += scale * (ds.T @ qi)
+                dv[b, :, g] += p.T @ doi
+    return dk, dv

@@ -121,6 +121,12 @@ def test_workspace_sizes():
     slots = 4 * 64 * 547
     assert ws(torch.bfloat16, 4, 64, 1, 576, 512, 2, 131072, full=True) == \
         -(-slots * 512 * 2 // 256) * 256 + slots * 4
+    # full decode with many (sequence, head) rows: splits stay at most 8,192
+    # tokens, so a 1M-token context is cut into 128 splits per row instead of
+    # one work-group walking all of it
+    slots = 65 * 16 * 128
+    assert ws(torch.bfloat16, 65, 16, 16, 128, 128, 128, 8192, full=True) == \
+        -(-slots * 128 * 4 // 256) * 256 + slots * 4
     assert ws(torch.bfloat16, 1, 4, 3, 128, 128, 128, 8) == 0          # invalid heads
     assert ws(torch.bfloat16, 1, 4, 4, 128, 128, 128, 8, local=0) == 0
 

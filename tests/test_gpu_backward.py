@@ -141,9 +141,12 @@ def _head_slice(t, heads):
     return host(t[:, :, heads].contiguous())
 
 
-def _sampled_full_size(cfg, q_tiles, k_tiles, heads):
+def _sampled_full_size(cfg, q_tiles, k_tiles, heads, sink_head=None):
     """Backward at a full workload's shape, checked on sampled tiles of the
-    given heads (GQA-free shapes: query head h reads kv head h)."""
+    given heads (GQA-free shapes: query head h reads kv head h). With
+    sink_head, the first key tile (the sink keys, attended by every row) of
+    that head is checked element by element against the oracle over all rows:
+    that tile's dk / dv are the chunked partial sums of the finalize launch."""
     pattern = inputs.PATTERN
     b, l = pattern["block"], pattern["local"]
     N = cfg.N
@@ -166,6 +169,14 @@ def _sampled_full_size(cfg, q_tiles, k_tiles, heads):
                                     rows=np.arange(k0, r1))
         assert_grad_parity(dk[:, k0:k1][:, :, heads], rk[:, k0:k1], f"{cfg.name} dk tile {t}")
         assert_grad_parity(dv[:, k0:k1][:, :, heads], rv[:, k0:k1], f"{cfg.name} dv tile {t}")
+    if sink_head is not None:
+        hs = [sink_head]
+        qs_, ks_, vs_, ds_ = (_head_slice(t, hs) for t in (q, k, v, do))
+        k1 = min(N, 128)
+        rk, rv = oracle.backward_keys(qs_, ks_, vs_, ds_, np.arange(k1), **pattern, scale=cfg.scale)
+        assert_grad_parity(dk[:, :k1][:, :, hs], rk, f"{cfg.name} dk sink tile, head {sink_head}")
+        assert_grad_parity(dv[:, :k1][:, :, hs], rv, f"{cfg.name} dv sink tile, head {sink_head}")
+        del rk, rv
     # Sums that hold at any size (the sink rows included), per kv head, in
     # double on the device, one head at a time.
     for h in range(cfg.Hkv):
@@ -188,4 +199,4 @@ def test_full_size_32k_sampled():
 def test_full_size_256k_sampled():
     """The 256K, 64-head, d_qk=192 / d_v=128 workload."""
     _sampled_full_size(inputs.PREFILL_BF16_256K, q_tiles=[0, 8, 1024, 2047],
-                       k_tiles=[1, 1023, 2047], heads=[0, 63])
+                       k_tiles=[1, 1023, 2047], heads=[0, 63], sink_head=0)

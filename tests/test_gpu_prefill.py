@@ -66,6 +66,11 @@ SMALL = [
     # general copy (their window starts one block later)
     (torch.bfloat16, 1, 3000, 2, 2, 128, 128, (64, 1, 16)),
     (torch.bfloat16, 1, 3000, 2, 1, 64, 64, (192, 1, 5)),       # window starts inside a tile
+    # d_qk = 192 visits the whole local sub-tile pairs in a rotated order;
+    # with blocks that are not 128 the rotation meets the loop copy without
+    # masks and the general one in the same tile
+    (torch.bfloat16, 1, 1700, 2, 2, 192, 128, (64, 1, 16)),
+    (torch.bfloat16, 1, 1900, 2, 2, 192, 128, (100, 2, 5)),
     (torch.float32, 1, 1300, 2, 2, 128, 128, (128, 1, 7)),
     (torch.float32, 2, 700, 4, 2, 64, 64, (32, 2, 3)),
 ]
@@ -116,10 +121,10 @@ def test_bf16_32k_sampled_tiles():
 
 
 def test_bf16_256k_stratified_sample():
-    """Every head; query blocks 0..8, 1023, 1024, 2047 and 8 seeded random blocks."""
+    """Every head; query blocks 0..8, 1023, 1024, 2047 and 32 seeded random blocks."""
     cfg = inputs.PREFILL_BF16_256K
     q, k, v = inputs.prefill_inputs(cfg, DEV)
-    tiles = _sample_tiles(cfg.N // 128, list(range(9)) + [1023, 1024, 2047], 8, 4)
+    tiles = _sample_tiles(cfg.N // 128, list(range(9)) + [1023, 1024, 2047], 32, 4)
     rows = np.concatenate([np.arange(t * 128, (t + 1) * 128) for t in tiles])
     _run_and_check(q, k, v, inputs.PATTERN, cfg.scale, rows=rows, what=cfg.name)
 

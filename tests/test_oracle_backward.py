@@ -198,3 +198,39 @@ def test_backward_rejects_bad_arguments():
         oracle.backward(x, x, x, x, block=2, sink=1, local=1, scale=1.0, rows=[-1])
     with pytest.raises(ValueError):
         oracle.backward(x, x, x, np.zeros((1, 4, 1, 3), np.float32), block=2, scale=1.0)
+
+
+@pytest.mark.parametrize("seed,b,s,l,N,Hq,Hkv,keys", [
+    (0, 4, 1, 2, 37, 2, 1, [0, 1, 2, 3]),                 # the sink block
+    (1, 8, 2, 3, 61, 4, 2, [0, 9, 15, 16, 30, 60]),       # sink, local and last keys
+    (2, 5, 0, 2, 23, 3, 3, [4, 5, 22]),                   # no sink
+    (3, 16, 1, 7, 150, 2, 2, list(range(16))),
+])
+def test_backward_keys_matches_autograd_of_bruteforce(seed, b, s, l, N, Hq, Hkv, keys):
+    """The key-side gradient (dk, dv of chosen keys from all their rows,
+    through the forward's lse and output) against float64 autograd of the
+    dense block-set mask, and against the full backward's dk / dv."""
+    rng = np.random.default_rng(300 + seed)
+    d_qk, d_v = 12, 8
+    q, k = _rand(rng, 1, N, Hq, d_qk), _rand(rng, 1, N, Hkv, d_qk)
+    v, do = _rand(rng, 1, N, Hkv, d_v), _rand(rng, 1, N, Hq, d_v)
+    scale = 0.41
+    dk, dv = oracle.backward_keys(q, k, v, do, keys, block=b, sink=s, local=l, scale=scale)
+    _, rk, rv = _autograd_reference(q[0], k[0], v[0], do[0], block_set_mask(N, b, s, l), scale)
+    np.testing.assert_allclose(dk[0], rk[keys], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv[0], rv[keys], rtol=0, atol=1e-11)
+    _, ok, ov = oracle.backward(q, k, v, do, block=b, sink=s, local=l, scale=scale)
+    np.testing.assert_allclose(dk[0], ok[0, keys], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv[0], ov[0, keys], rtol=0, atol=1e-11)
+
+
+def test_backward_keys_bf16_bits():
+    rng = np.random.default_rng(310)
+    N, Hq, Hkv, d_qk, d_v = 300, 2, 1, 16, 8
+    q, k = f32_to_bf16_bits(_rand(rng, 1, N, Hq, d_qk)), f32_to_bf16_bits(_rand(rng, 1, N, Hkv, d_qk))
+    v, do = f32_to_bf16_bits(_rand(rng, 1, N, Hkv, d_v)), f32_to_bf16_bits(_rand(rng, 1, N, Hq, d_v))
+    keys = list(range(0, 32)) + [200, 299]
+    dk, dv = oracle.backward_keys(q, k, v, do, keys, block=32, sink=1, local=3, scale=0.25)
+    _, ok, ov = oracle.backward(q, k, v, do, block=32, sink=1, local=3, scale=0.25)
+    np.testing.assert_allclose(dk[0], ok[0, keys], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv[0], ov[0, keys], rtol=0, atol=1e-11)
