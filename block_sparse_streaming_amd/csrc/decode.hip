@@ -134,8 +134,17 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
 
     const int split = blockIdx.x, g = blockIdx.y, bb = blockIdx.z;
     const int tid = threadIdx.x, tg = tid / kTpt, tl = tid % kTpt;
+    // A split slot past the row's splits holds lse = -inf, so the merge needs
+    // neither the context length nor the split count.
+    auto no_split = [&]() __attribute__((always_inline)) {
+        for (int hh = tid; hh < G; hh += kValuThreads)
+            a.ws_lse[((int64_t)bb * a.Hq + g * G + hh) * a.plan.max_splits + split] = -INFINITY;
+    };
     const int64_t L = row_context(a, bb);
-    if (L <= 0) return;
+    if (L <= 0) {
+        no_split();
+        return;
+    }
     const Sel sel = select_tokens(L, a);
     // Splits [0, n_win) cover the window's positions; the next list_splits(a)
     // cover the listed tokens (hybrid decode), positions of the list.
@@ -143,7 +152,10 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
     const bool listed = kList && split >= n_win;
     const int64_t p_begin = (int64_t)(listed ? split - n_win : split) * a.plan.split_tokens;
     const int64_t p_lim = listed ? (int64_t)a.topk_k : sel.total;
-    if (p_begin >= p_lim) return;
+    if (p_begin >= p_lim) {
+        no_split();
+        return;
+    }
     const int64_t p_end = p_begin + a.plan.split_tokens < p_lim ? p_begin + a.plan.split_tokens : p_lim;
     // Positions and tokens fit in 32 bits (context lengths are int32).
     const uint32_t up_end = (uint32_t)p_end, ur1 = (uint32_t)sel.r1_end, ur2 = (uint32_t)sel.r2_begin;
@@ -355,9 +367,19 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, kg = lane >> 4;
+    const int heads_here = a.group - hc * 64 < 64 ? a.group - hc * 64 : 64;
+    // A split slot past the row's splits holds lse = -inf, so the merge needs
+    // neither the context length nor the split count.
+    auto no_split = [&]() __attribute__((always_inline)) {
+        for (int h = tid; h < heads_here; h += kLatThreads)
+            a.ws_lse[((int64_t)bb * a.Hq + g * a.group + hc * 64 + h) * a.plan.max_splits + split] = -INFINITY;
+    };
 
     const int64_t L = row_context(a, bb);
-    if (L <= 0) return;
+    if (L <= 0) {
+        no_split();
+        return;
+    }
     const Sel sel = select_tokens(L, a);
     // Splits [0, n_win) cover the window's positions; the next list_splits(a)
     // cover the listed tokens (hybrid decode), positions of the list.
@@ -365,7 +387,10 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     const bool listed = split >= n_win;
     const int64_t p_begin = (int64_t)(listed ? split - n_win : split) * a.plan.split_tokens;
     const int64_t p_lim = listed ? (int64_t)a.topk_k : sel.total;
-    if (p_begin >= p_lim) return;
+    if (p_begin >= p_lim) {
+        no_split();
+        return;
+    }
     const int64_t p_end = p_begin + a.plan.split_tokens < p_lim ? p_begin + a.plan.split_tokens : p_lim;
     const int ntok = (int)(p_end - p_begin);
     const int nch = (ntok + kLatCh - 1) / kLatCh;
@@ -385,7 +410,6 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
         for (int t = tid; t < n1 + n2; t += kLatThreads)
             pids[t] = a.page_table[seq * a.max_pages + (t < n1 ? lp1 + t : lp2 + (t - n1))];
 
-    const int heads_here = a.group - hc * 64 < 64 ? a.group - hc * 64 : 64;
     const bool active = wave * 16 < heads_here;
     const int head = g * a.group + hc * 64 + wave * 16 + l16;  // this lane's query head
 
@@ -637,7 +661,6 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * (kMergeThreads / 64) + (threadIdx.x >> 6);  // bb * Hq + h
     if (row >= a.B * a.Hq) return;
-    const int bb = row / a.Hq;
     Elem *out = (Elem *)a.o + (int64_t)row * D + E * lane;
     const int64_t slot0 = (int64_t)row * a.plan.max_splits;
     const float *wl = a.ws_lse + slot0;
@@ -675,32 +698,27 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
             }
         }
     };
-    // The first batch of partial rows and the lse of the first 64 splits are
-    // requested before the row's split count is known (it needs the context
-    // length): the slots exist for every row. Slots past the count hold
-    // stale values; they are never used (selects and uniform branches below,
-    // not products with a zero weight).
-    const int nb0 = a.plan.max_splits < 64 ? a.plan.max_splits : 64;
+    // Every split slot of the row holds an lse: -inf for a slot past the
+    // row's splits (or a split with no attended key), so the split count and
+    // the context length are not needed, and the first batch of partial rows
+    // is requested together with the lse of the first 64 splits. A slot with
+    // a zero weight may hold a stale partial row: it never enters a product
+    // (uniform branches below, not multiplications by zero).
+    const int ns = a.plan.max_splits;
+    const int nb0 = ns < 64 ? ns : 64;
     load_batch(0, nb0);
     const float lse0 = lane < nb0 ? wl[lane] : -INFINITY;
-
-    const int64_t L = row_context(a, bb);
-    int ns = 0;
-    if (L > 0) {
-        const Sel sel = select_tokens(L, a);
-        ns = (int)((sel.total + a.plan.split_tokens - 1) / a.plan.split_tokens) + list_splits(a);
-    }
-    if (ns == 0) {
+    float M = lse0;
+    for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, wl[s]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (M == -INFINITY) {  // no key at all (context length 0)
 #pragma unroll
         for (int e = 0; e < E; ++e) out[e] = Elem(0);
         if (lane == 0 && a.lse) a.lse[row] = -INFINITY;
         return;
     }
-    float M = lane < ns ? lse0 : -INFINITY;
-    for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, wl[s]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float Z = lane < ns ? fast_exp2(lse0 - M) : 0.f;
+    float Z = fast_exp2(lse0 - M);
     for (int s = lane + 64; s < ns; s += 64) Z += fast_exp2(wl[s] - M);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) Z += __shfl_xor(Z, o);
@@ -711,14 +729,15 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge(const DecodeArgs a
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
     for (int s64 = 0; s64 < ns; s64 += 64) {
         const float lw = s64 == 0 ? lse0 : (s64 + lane < ns ? wl[s64 + lane] : -INFINITY);
-        const float wlane = s64 + lane < ns ? fast_exp2(lw - M) * inv : 0.f;
+        const float wlane = fast_exp2(lw - M) * inv;
+        const uint64_t used = __builtin_amdgcn_ballot_w64(wlane != 0.f);
         const int nb = ns - s64 < 64 ? ns - s64 : 64;
-        if (s64 > 0) load_batch(0, nb);
         for (int s0 = 0; s0 < nb; s0 += kMergeBatch) {
-            if (s0 > 0) load_batch(s0, nb);
+            if (!((used >> s0) & ((1u << kMergeBatch) - 1))) continue;  // uniform: no weight here
+            if (s0 > 0 || s64 > 0) load_batch(s0, nb);
 #pragma unroll
             for (int u = 0; u < kMergeBatch; ++u) {
-                if (s0 + u < nb) {  // uniform
+                if (s0 + u < nb && ((used >> (s0 + u)) & 1)) {  // uniform
                     const float wf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlane), s0 + u));
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(wf, part[u][e], acc[e]);

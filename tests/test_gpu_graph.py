@@ -37,7 +37,7 @@ def _calls(kind):
     if kind in ("ssa", "full"):
         inp = _latent((5000, 130, 2049, 777), (1, 1, 1, 1), seed)
         full = kind == "full"
-        ws = torch.empty(ssa.decode_workspace_size(torch.bfloat16, 4, 64, 1, 576, 512, inputs.PAGE_SIZE,
+        ws = torch.zeros(ssa.decode_workspace_size(torch.bfloat16, 4, 64, 1, 576, 512, inputs.PAGE_SIZE,
                                                    inp.page_table.shape[1], full=full),
                          dtype=torch.uint8, device=DEV)
         insts = _instances(inp, 3, seed)
@@ -51,11 +51,26 @@ def _calls(kind):
             else:
                 ssa.decode(q, inp.k_cache, inp.v_cache, table, inp.ctx_lens, **inputs.PATTERN,
                            scale=LAT_SCALE, out=outs[r], workspace=ws)
+    elif kind == "valu":
+        # MHA / GQA shapes: the split kernel merges each row itself, through
+        # arrival counters in the workspace that every call leaves at zero.
+        inp = inputs.extend_inputs((5000, 130, 2049, 777), (1, 1, 1, 1), 8, 4, 128, 128, torch.bfloat16, DEV,
+                                   seed)
+        ws = torch.zeros(ssa.decode_workspace_size(torch.bfloat16, 4, 8, 4, 128, 128, inputs.PAGE_SIZE,
+                                                   inp.page_table.shape[1]),
+                         dtype=torch.uint8, device=DEV)
+        insts = _instances(inp, 3, seed)
+        outs = [torch.empty((4, 8, 128), dtype=torch.bfloat16, device=DEV) for _ in insts]
+
+        def call(r):
+            q, table, _ = insts[r]
+            ssa.decode(q, inp.k_cache, inp.v_cache, table, inp.ctx_lens, **inputs.PATTERN,
+                       scale=128 ** -0.5, out=outs[r], workspace=ws)
     elif kind == "hybrid":
         inp = _latent((5000, 3000, 2049, 1500), (1, 1, 1, 1), seed)
         pat = dict(block=1, sink=16, local=1024)
         K = 256
-        ws = torch.empty(ssa.hybrid_decode_workspace_size(torch.bfloat16, 4, 64, 1, 576, 512, inputs.PAGE_SIZE,
+        ws = torch.zeros(ssa.hybrid_decode_workspace_size(torch.bfloat16, 4, 64, 1, 576, 512, inputs.PAGE_SIZE,
                                                           inp.page_table.shape[1], K, **pat),
                          dtype=torch.uint8, device=DEV)
         insts = _instances(inp, 3, seed, lists_k=K)
@@ -76,7 +91,7 @@ def _calls(kind):
         Hq, Hkv, dqk, dv = inp.q.shape[1], inp.k_cache.shape[2], inp.q.shape[2], inp.v_cache.shape[3]
         ws_bytes = ssa.extend_workspace_size(torch.bfloat16, len(inp.lens), total_q, max_q, Hq, Hkv, dqk, dv,
                                              inputs.PAGE_SIZE, inp.page_table.shape[1])
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=DEV)
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=DEV)
         insts = _instances(inp, 3, seed)
         outs = [torch.empty((total_q, Hq, dv), dtype=torch.bfloat16, device=DEV) for _ in insts]
         scale = LAT_SCALE if kind == "mtp" else dqk ** -0.5
@@ -89,7 +104,7 @@ def _calls(kind):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("kind", ["ssa", "full", "hybrid", "mtp", "chunk"])
+@pytest.mark.parametrize("kind", ["ssa", "full", "valu", "hybrid", "mtp", "chunk"])
 def test_graph_replays_match_eager(kind):
     call, outs, n = _calls(kind)
     say("graph", kind)
