@@ -21,7 +21,7 @@ SSA_BF16 = 1
 
 # Exported symbols, in the order include/ssa.h declares them.
 EXPORTS = ("ssa_prefill", "ssa_prefill_dual", "ssa_prefill_backward", "ssa_prefill_backward_workspace_size",
-           "ssa_decode", "full_attn_decode", "ssa_decode_workspace_size", "ssa_extend",
+           "ssa_decode", "ssa_decode_noalloc", "full_attn_decode", "ssa_decode_workspace_size", "ssa_extend",
            "ssa_extend_workspace_size", "hybrid_decode", "hybrid_decode_workspace_size",
            "ssa_status_string")
 
@@ -73,6 +73,9 @@ def load_library() -> ctypes.CDLL:
     lib.full_attn_decode.restype = ctypes.c_int
     lib.full_attn_decode.argtypes = [ctypes.c_int, p, p, p, i64p, i64p, p, i32, p, i32, i32, i32,
                                      i32, i32, i32, p, p, p, sz, f32, p]
+    lib.ssa_decode_noalloc.restype = ctypes.c_int
+    lib.ssa_decode_noalloc.argtypes = [ctypes.c_int, p, p, p, i64p, i64p, p, i32, p, i32, i32, i32, i32,
+                                       i32, i32, p, p, Pattern, f32, p]
     lib.ssa_decode_workspace_size.restype = sz
     lib.ssa_decode_workspace_size.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32,
                                               Pattern, ctypes.c_int]
@@ -268,7 +271,7 @@ def decode_workspace_size(dtype: torch.dtype, batch: int, heads_q: int, heads_kv
 
 
 def _decode(full: bool, q, k_cache, v_cache, page_table, ctx_lens, *, block, sink, local, scale,
-            out, workspace, return_lse):
+            out, workspace, return_lse, noalloc: bool = False):
     lib = load_library()
     _on_gpu(q, k_cache, v_cache, page_table, ctx_lens)
     dt = _dtype_code(q)
@@ -291,13 +294,19 @@ def _decode(full: bool, q, k_cache, v_cache, page_table, ctx_lens, *, block, sin
     elif out.shape != (B, Hq, d_v) or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B, Hq, d_v] tensor of q's dtype")
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    if noalloc:
+        _check(lib.ssa_decode_noalloc(dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _strides3(k_cache),
+                                      _strides3(v_cache), _ptr(page_table), max_pages, _ptr(ctx_lens), B,
+                                      Hq, Hkv, d_qk, d_v, page_size, _ptr(out), _ptr(lse),
+                                      Pattern(block, sink, local), float(scale), _stream(q.device)))
+        return (out, lse) if return_lse else out
     need = decode_workspace_size(q.dtype, B, Hq, Hkv, d_qk, d_v, page_size, max_pages, block=block,
                                  sink=sink, local=local, full=full)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _on_gpu(workspace)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d_qk)
     ws_bytes = workspace.numel() * workspace.element_size()
     common = (dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _strides3(k_cache), _strides3(v_cache),
               _ptr(page_table), max_pages, _ptr(ctx_lens), B, Hq, Hkv, d_qk, d_v, page_size,
@@ -316,6 +325,14 @@ def decode(q, k_cache, v_cache, page_table, ctx_lens, *, block: int = 128, sink:
     [B, max_pages] int32; ctx_lens [B] int32 (the new token included)."""
     return _decode(False, q, k_cache, v_cache, page_table, ctx_lens, block=block, sink=sink,
                    local=local, scale=scale, out=out, workspace=workspace, return_lse=return_lse)
+
+
+def decode_noalloc(q, k_cache, v_cache, page_table, ctx_lens, *, block: int = 128, sink: int = 1,
+                   local: int = 7, scale: float | None = None, out=None, return_lse: bool = False):
+    """ssa_decode_noalloc: ``decode`` in the library's fixed per-GPU scratch
+    (no workspace argument; the library allocates nothing)."""
+    return _decode(False, q, k_cache, v_cache, page_table, ctx_lens, block=block, sink=sink,
+                   local=local, scale=scale, out=out, workspace=None, return_lse=return_lse, noalloc=True)
 
 
 def full_decode(q, k_cache, v_cache, page_table, ctx_lens, *, scale: float | None = None, out=None,

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
 
 #include "ssa.h"
 #include "kernels.h"
@@ -129,13 +130,47 @@ WorkspaceLayout workspace_layout(int32_t batch, int32_t heads_q, int32_t d_v, co
     return w;
 }
 
+// Scratch of ssa_decode_noalloc: a fixed device array, one copy on each GPU
+// the library runs on, held until the process ends. Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// device symbol): it takes the device address that hipGetSymbolAddress
+// returns, found once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the scratch on the device `stream` runs on; null on a
+// HIP failure.
+void *device_scratch(hipStream_t stream) {
+    int dev = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+        void *p = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (err != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// Checks, plans and launches a decode-family call. With noalloc the
+// workspace arguments are ignored and the call runs in the device scratch
+// above (after every argument check, and only if it fits there).
 ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
                          const int64_t k_strides[3], const int64_t v_strides[3],
                          const int32_t *page_table, int32_t max_pages, const int32_t *ctx_lens,
                          int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t d_qk, int32_t d_v,
                          int32_t page_size, void *o, float *lse, void *workspace,
                          size_t workspace_bytes, ssa_pattern pattern, float scale, bool full,
-                         hipStream_t stream, const int32_t *topk = nullptr, int32_t topk_k = 0) {
+                         hipStream_t stream, const int32_t *topk = nullptr, int32_t topk_k = 0,
+                         bool noalloc = false) {
     if (!dtype_ok(dtype)) return SSA_ERR_INVALID_ARG;
     if (topk_k < 0 || (topk_k > 0 && !topk && batch > 0)) return SSA_ERR_INVALID_ARG;
     if (batch < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv || d_qk < 1 || d_v < 1 ||
@@ -167,7 +202,13 @@ ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, co
         (int64_t)plan.max_splits * heads_kv * plan.head_chunks * batch > kInt32Max)  // linear work-group ids
         return SSA_ERR_UNSUPPORTED;
     const WorkspaceLayout wl = workspace_layout(batch, heads_q, d_v, plan);
-    if (!workspace || !aligned16(workspace) || workspace_bytes < wl.total) return SSA_ERR_WORKSPACE;
+    if (noalloc) {
+        if (wl.total > kNoAllocScratchBytes) return SSA_ERR_WORKSPACE;
+        workspace = device_scratch(stream);
+        if (!workspace) return SSA_ERR_HIP;
+    } else if (!workspace || !aligned16(workspace) || workspace_bytes < wl.total) {
+        return SSA_ERR_WORKSPACE;
+    }
 
     DecodeArgs a{};
     a.q = q;
@@ -491,6 +532,17 @@ ssa_status ssa_decode(ssa_dtype dtype, const void *q, const void *k_cache, const
     return decode_common(dtype, q, k_cache, v_cache, k_strides, v_strides, page_table, max_pages,
                          ctx_lens, batch, heads_q, heads_kv, d_qk, d_v, page_size, o, lse, workspace,
                          workspace_bytes, pattern, scale, false, stream);
+}
+
+ssa_status ssa_decode_noalloc(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
+                              const int64_t k_strides[3], const int64_t v_strides[3],
+                              const int32_t *page_table, int32_t max_pages, const int32_t *ctx_lens,
+                              int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t d_qk,
+                              int32_t d_v, int32_t page_size, void *o, float *lse, ssa_pattern pattern,
+                              float scale, hipStream_t stream) {
+    return decode_common(dtype, q, k_cache, v_cache, k_strides, v_strides, page_table, max_pages,
+                         ctx_lens, batch, heads_q, heads_kv, d_qk, d_v, page_size, o, lse, nullptr, 0,
+                         pattern, scale, false, stream, nullptr, 0, true);
 }
 
 ssa_status full_attn_decode(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,

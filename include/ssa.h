@@ -219,6 +219,34 @@ ssa_status ssa_decode(ssa_dtype dtype, const void *q, const void *k_cache, const
                       hipStream_t stream);
 
 /*
+ * ssa_decode_noalloc - ssa_decode for callers that cannot allocate: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid device
+ * allocation. Same arguments, layouts, checks and results as ssa_decode,
+ * without the workspace: the call runs in a fixed scratch array of 32 MiB
+ * (33,554,432 bytes) compiled into the library, one copy per GPU, held until
+ * the process ends. The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); on its first use on
+ * a device it looks up that device's copy of the array (hipGetSymbolAddress,
+ * with the device current), and after that it makes no HIP call other than
+ * the launches.
+ *
+ * A call whose ssa_decode_workspace_size(...) exceeds the scratch returns
+ * SSA_ERR_WORKSPACE and launches nothing (the 128K-context latent batch of
+ * 32 sequences needs 16.8 MB; 65 sequences x 16 heads at d = 128, 4.3 MB).
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (no call needs initial contents): calls that overlap on one
+ * GPU (other streams, other threads) race and give wrong results. The
+ * device is the one `stream` belongs to. SSA_ERR_HIP if the scratch cannot
+ * be found on it.
+ */
+ssa_status ssa_decode_noalloc(ssa_dtype dtype, const void *q, const void *k_cache, const void *v_cache,
+                              const int64_t k_strides[3], const int64_t v_strides[3],
+                              const int32_t *page_table, int32_t max_pages, const int32_t *ctx_lens,
+                              int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t d_qk,
+                              int32_t d_v, int32_t page_size, void *o, float *lse, ssa_pattern pattern,
+                              float scale, hipStream_t stream);
+
+/*
  * full_attn_decode - the dense comparator of the digest's section 02
  * efficiency figure: the same call as ssa_decode, attending to every token
  * 0..L-1 of the context. Same layouts, ownership, errors and compiled shapes.

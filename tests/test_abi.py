@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import block_sparse_streaming_amd as ssa
 
@@ -82,6 +83,30 @@ def decode_call(full=False, dtype=1, B=2, Hq=4, Hkv=4, dqk=128, dv=128, ps=128, 
     if full:
         return lib.full_attn_decode(*args, 0.1, None)
     return lib.ssa_decode(*args, ssa.Pattern(*pattern), 0.1, None)
+
+
+def noalloc_call(dtype=1, B=2, Hq=4, Hkv=4, dqk=128, dv=128, ps=128, max_pages=8, pattern=(128, 1, 7),
+                 ptr=FAKE):
+    lib = ssa.load_library()
+    ks = strides(ps * Hkv * dqk, Hkv * dqk, dqk)
+    p = ctypes.c_void_p(ptr) if ptr is not None else None
+    return lib.ssa_decode_noalloc(dtype, p, p, p, ks, ks, p, max_pages, p, B, Hq, Hkv, dqk, dv, ps, p, None,
+                                  ssa.Pattern(*pattern), 0.1, None)
+
+
+def test_decode_noalloc_validation():
+    """The no-allocation decode checks its arguments like ssa_decode, on the
+    host, before any HIP call (these run without a GPU), and rejects a call
+    whose workspace would not fit its fixed 32 MiB scratch."""
+    assert noalloc_call(dtype=3) == INVALID
+    assert noalloc_call(Hq=6, Hkv=4) == INVALID
+    assert noalloc_call(ptr=None) == INVALID
+    assert noalloc_call(pattern=(128, 1, 0)) == INVALID
+    assert noalloc_call(dqk=96, dv=96) == UNSUPPORTED
+    assert noalloc_call(B=0, ptr=None) == OK
+    # 200 sequences x 64 heads, d = 128: 8 splits of fp32 partials, 52 MB
+    assert ssa.decode_workspace_size(torch.bfloat16, 200, 64, 64, 128, 128, 128, 8) > 32 << 20
+    assert noalloc_call(B=200, Hq=64, Hkv=64) == WORKSPACE
 
 
 @pytest.mark.parametrize("full", [False, True])
