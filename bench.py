@@ -131,7 +131,13 @@ def measure_ceilings():
     return MEASURED
 
 
+TRAFFIC_SOURCE = ("recorded, not measured in this run: profiles/traffic.json, HBM bytes per launch from "
+                  "rocprofv3 FETCH_SIZE and WRITE_SIZE runs (copy-calibrated), kept only while the "
+                  "kernel's sources hash to the recorded SHA-256")
+
+
 def with_measured(roof: dict) -> dict:
+    roof["traffic_source"] = TRAFFIC_SOURCE if roof.get("traffic") is not None else None
     key = "bf16_gemm_tflops" if roof["unit"] == "TFLOP/s" else "hbm_read_gbs"
     if key in MEASURED and not (roof["unit"] == "TFLOP/s" and roof["peak"] != PEAK_BF16_TFLOPS):
         roof["measured_peak"] = MEASURED[key]
@@ -682,30 +688,224 @@ def bench_decode_ragged(iters: int):
 # ---------------------------------------------------------------------------
 # CPU oracle
 # ---------------------------------------------------------------------------
-def cpu_baseline():
-    """The CPU oracle, as it stands, on the prefill workload: every query tile
-    of every head (the whole workload is a few seconds of fp64 work on the
-    host cores, inside the bounded budget), drawn on the CPU with the same
-    distribution and dtype."""
+def cpu_info() -> dict:
+    """The host the oracle runs on: CPU model (from /proc/cpuinfo) and the
+    number of CPUs this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return {"cpu_model": model, "nproc": nproc}
+
+
+def _bits(t):
+    """Host array for the oracle: bf16 bit patterns as uint16, or float32."""
+    import torch
+    t = t.contiguous()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def _cpu_randn(shape, dtype, gen):
+    import torch
+    return torch.randn(shape, generator=gen).to(dtype)
+
+
+_ORACLE_THREADS = []   # the oracle's thread count before any change (all cores)
+
+
+def _oracle_seconds(threads: int, fn) -> float:
+    """Seconds of fn() with the oracle on `threads` threads (0: all)."""
+    import oracle
+    if not _ORACLE_THREADS:
+        _ORACLE_THREADS.append(oracle.max_threads())
+    oracle.set_threads(threads if threads > 0 else _ORACLE_THREADS[0])
+    try:
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+    finally:
+        oracle.set_threads(_ORACLE_THREADS[0])
+
+
+def _prefill_oracle(cfg, heads: int, rows, gen):
+    """A callable running the oracle on `rows` of `heads` query heads of the
+    workload's shape (inputs drawn on the CPU, same distribution and dtype),
+    and the attended (query, key) pairs it evaluates."""
+    import oracle
+    from block_sparse_streaming_amd import inputs
+    q = _bits(_cpu_randn((cfg.B, cfg.N, heads, cfg.d_qk), cfg.dtype, gen))
+    k = _bits(_cpu_randn((cfg.B, cfg.N, heads, cfg.d_qk), cfg.dtype, gen))
+    v = _bits(_cpu_randn((cfg.B, cfg.N, heads, cfg.d_v), cfg.dtype, gen))
+    pat = inputs.PATTERN
+    b, s, l = pat["block"], pat["sink"], pat["local"]
+    r = np.arange(cfg.N) if rows is None else np.asarray(rows)
+    lo = np.maximum(s * b, (r // b - l + 1) * b)
+    pairs = int((np.minimum(s * b, r + 1) + np.maximum(0, r + 1 - lo)).sum()) * heads * cfg.B
+    return (lambda: oracle.prefill(q, k, v, **pat, scale=cfg.scale, rows=rows)), pairs
+
+
+def _decode_oracle(cfg, lens, full: bool, gen):
+    """A callable running the paged decode oracle on sequences of context
+    lengths `lens` (the workload's heads and dims; a host cache holding only
+    the pages the call reads, in shuffled order), and the attended tokens."""
+    import oracle
+    from block_sparse_streaming_amd import inputs
+    pat = inputs.PATTERN
+    P = inputs.PAGE_SIZE
+    b, s, l = pat["block"], pat["sink"], pat["local"]
+    need, toks = [], 0
+    for L in lens:
+        j = np.arange(L)
+        keep = np.ones(L, bool) if full else (j // b < s) | (j // b > (L - 1) // b - l)
+        need.append(np.unique(j[keep] // P))
+        toks += int(keep.sum())
+    n = sum(x.size for x in need)
+    perm = np.random.default_rng(cfg.seed).permutation(n).astype(np.int32)
+    max_pages = max(-(-L // P) for L in lens)
+    table = np.full((len(lens), max_pages), 0, np.int32)
+    off = 0
+    for i, x in enumerate(need):
+        table[i, x] = perm[off:off + x.size]
+        off += x.size
+    q = _bits(_cpu_randn((len(lens), cfg.Hq, cfg.d_qk), cfg.dtype, gen))
+    kc = _bits(_cpu_randn((n, P, cfg.Hkv, cfg.d_qk), cfg.dtype, gen))
+    vc = kc[..., :cfg.d_v] if cfg.latent else _bits(_cpu_randn((n, P, cfg.Hkv, cfg.d_v), cfg.dtype, gen))
+    kw = dict(block=1, sink=0, local=1) if full else pat
+    lens_np = np.asarray(lens, np.int32)
+    return (lambda: oracle.decode_paged(q, kc, vc, table, lens_np, **kw, scale=cfg.scale, full=full)), toks
+
+
+def _entry(what, sample, scale_to_full, seconds_all, seconds_one, work_full, unit, per_unit, threads,
+           scale_one=None):
+    """One workload's oracle timing: the sample's seconds on all cores and on
+    one core, the time for the whole workload they imply (linear in work) and
+    the rate in the metric's unit. scale_one: the one-core sample's own
+    factor, when it is another sample."""
+    full_all = seconds_all * scale_to_full
+    full_one = seconds_one * (scale_to_full if scale_one is None else scale_one)
+    return {"what": what, "sample": sample, "work_full": work_full,
+            "all_cores": {"threads": threads, "sample_s": seconds_all, "full_s": full_all,
+                          unit: work_full * per_unit / full_all},
+            "one_core": {"threads": 1, "sample_s": seconds_one, "full_s": full_one,
+                         unit: work_full * per_unit / full_one},
+            "unit": unit}
+
+
+def cpu_baseline(full_runs: bool = False):
+    """The CPU oracle, as it stands, timed on this host with all cores and
+    with one core, for each workload of the metric. The headline value is the
+    32K prefill on all cores over the whole workload (a few seconds). The
+    other figures come from bounded samples of each workload (rows of some
+    query heads for prefill, sequences for decode; the oracle's cost is linear
+    in attended pairs or tokens, so a sample scales to the workload exactly),
+    except with full_runs, where prefill at 2K and 32K and decode on the latent
+    and ragged workloads run whole (the 256K prefill is always sampled)."""
     import torch
     import oracle
     from block_sparse_streaming_amd import inputs
 
+    gen = torch.Generator().manual_seed(4040)
+    if not _ORACLE_THREADS:
+        _ORACLE_THREADS.append(oracle.max_threads())
+    threads = _ORACLE_THREADS[0]
+    table = {}
+
+    def flops(cfg):
+        return 2 * (cfg.d_qk + cfg.d_v)
+
+    # prefill fp32 2K: the whole workload both ways
+    cfg = inputs.PREFILL_FP32_2K
+    fn, pairs = _prefill_oracle(cfg, cfg.Hq, None, gen)
+    table[cfg.name] = _entry("ssa_prefill", "whole workload", 1.0, _oracle_seconds(0, fn),
+                             _oracle_seconds(1, fn), pairs, "TFLOP/s", flops(cfg) * 1e-12, threads)
+
+    # prefill bf16 32K: whole on all cores; one core on every 16th query tile
+    # (whole with full_runs)
     cfg = inputs.PREFILL_BF16_32K
-    pat = inputs.PATTERN
-    gen = torch.Generator().manual_seed(cfg.seed)
-    q = torch.randn((1, cfg.N, cfg.Hq, cfg.d_qk), generator=gen).to(cfg.dtype)
-    k = torch.randn((1, cfg.N, cfg.Hkv, cfg.d_qk), generator=gen).to(cfg.dtype)
-    v = torch.randn((1, cfg.N, cfg.Hkv, cfg.d_v), generator=gen).to(cfg.dtype)
-    qh, kh, vh = (t.view(torch.int16).numpy().view(np.uint16) for t in (q, k, v))
+    fn_all, pairs = _prefill_oracle(cfg, cfg.Hq, None, gen)
+    t_all = _oracle_seconds(0, fn_all)
+    if full_runs:
+        t_one, scale_one, sample = _oracle_seconds(1, fn_all), 1.0, "whole workload"
+    else:
+        rows = np.concatenate([np.arange(t * 128, t * 128 + 128) for t in range(0, cfg.N // 128, 16)])
+        fn1, pairs1 = _prefill_oracle(cfg, cfg.Hq, rows, gen)
+        t_one, scale_one = _oracle_seconds(1, fn1), pairs / pairs1
+        sample = "all cores: whole workload; one core: every 16th 128-row query tile, all heads"
+    headline = _entry("ssa_prefill", sample, 1.0, t_all, t_one, pairs, "TFLOP/s",
+                      flops(cfg) * 1e-12, threads, scale_one=scale_one)
+    table[cfg.name] = headline
+
+    # prefill bf16 256K: stratified rows (query tiles 0..8, 1023, 1024, 2047
+    # and 4 seeded random tiles) of 2 of the 64 heads
+    cfg = inputs.PREFILL_BF16_256K
+    rng = np.random.default_rng(7)
+    tiles = sorted(set(list(range(9)) + [1023, 1024, 2047] +
+                       [int(x) for x in rng.choice(np.arange(9, 2047), 4, replace=False)]))
+    rows = np.concatenate([np.arange(t * 128, t * 128 + 128) for t in tiles])
+    fn, pairs_s = _prefill_oracle(cfg, 2, rows, gen)
+    pairs_full = attended_pairs(cfg.N, **inputs.PATTERN) * cfg.Hq * cfg.B
+    t_all, t_one = _oracle_seconds(0, fn), _oracle_seconds(1, fn)
+    table[cfg.name] = _entry("ssa_prefill", f"{len(tiles)} query tiles x 2 of 64 heads "
+                             f"({pairs_s} of {pairs_full} pairs), extrapolated by pair count",
+                             pairs_full / pairs_s, t_all, t_one, pairs_full, "TFLOP/s",
+                             flops(cfg) * 1e-12, threads)
+
+    # latent decode at 128K: SSA on all 32 sequences both ways; full
+    # attention on one sequence (all 32 with full_runs)
+    cfg = inputs.DECODE_LATENT_128K
+    lens = cfg.lens
+    fn, toks = _decode_oracle(cfg, lens, False, gen)
+    nbytes = toks * cfg.d_qk * 2
+    table[cfg.name + ":ssa_decode"] = _entry(
+        "ssa_decode", "whole workload", 1.0, _oracle_seconds(0, fn), _oracle_seconds(1, fn), nbytes,
+        "GB/s", 1e-9, threads)
+    sub = lens if full_runs else lens[:1]
+    fn, toks_s = _decode_oracle(cfg, sub, True, gen)
+    toks_full = sum(lens)
+    table[cfg.name + ":full_attn_decode"] = _entry(
+        "full_attn_decode", "whole workload" if full_runs else
+        f"1 of {len(lens)} sequences, extrapolated by token count", toks_full / toks_s,
+        _oracle_seconds(0, fn), _oracle_seconds(1, fn), toks_full * cfg.d_qk * 2, "GB/s", 1e-9, threads)
+
+    # ragged decode: SSA on all 65 sequences both ways
+    cfg = inputs.DECODE_RAGGED
+    fn, toks = _decode_oracle(cfg, cfg.lens, False, gen)
+    table[cfg.name + ":ssa_decode"] = _entry(
+        "ssa_decode", "whole workload", 1.0, _oracle_seconds(0, fn), _oracle_seconds(1, fn),
+        toks * cfg.Hkv * (cfg.d_qk + cfg.d_v) * 2, "GB/s", 1e-9, threads)
+
+    info = cpu_info()
+    h = headline["all_cores"]
+    return {"value": h["TFLOP/s"], "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole 32K prefill workload ({h['full_s']:.1f} s of fp64 oracle work on "
+                      f"{threads} threads); per-workload figures, all cores and one core, in 'workloads'",
+            "cpu_model": info["cpu_model"], "nproc": info["nproc"], "workloads": table}
+
+
+def print_cpu_oracle_table():
+    """Markdown table of the oracle's times on this host (full runs)."""
     t0 = time.perf_counter()
-    oracle.prefill(qh, kh, vh, **pat, scale=cfg.scale)
-    elapsed = time.perf_counter() - t0
-    flops = attended_pairs(cfg.N, **pat) * cfg.Hq * cfg.B * 2 * (cfg.d_qk + cfg.d_v)
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"the whole prefill workload ({cfg.N // 128} query tiles x {cfg.Hq} heads), "
-                      f"{elapsed:.1f} s of fp64 oracle work"}
+    cpu = cpu_baseline(full_runs=True)
+    print(f"Host: {cpu['cpu_model']}, nproc {cpu['nproc']}, oracle threads {cpu['cores']} "
+          f"(all cores) and 1; {time.perf_counter() - t0:.0f} s in all.\n")
+    print("| workload | call | sample | all cores: s | all cores: rate | one core: s | one core: rate |")
+    print("|---|---|---|---|---|---|---|")
+    for name, e in cpu["workloads"].items():
+        u = e["unit"]
+        a, o = e["all_cores"], e["one_core"]
+        print(f"| {name.split(':')[0]} | {e['what']} | {e['sample']} | {a['full_s']:.2f} | "
+              f"{a[u] * (1e3 if u == 'TFLOP/s' else 1):.3f} {'GFLOP/s' if u == 'TFLOP/s' else u} | "
+              f"{o['full_s']:.2f} | {o[u] * (1e3 if u == 'TFLOP/s' else 1):.3f} "
+              f"{'GFLOP/s' if u == 'TFLOP/s' else u} |", flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -758,6 +958,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--profile", choices=["prefill", "prefill_fp32", "prefill_256k", "decode", "backward",
                                           "backward_256k", "dual", "extend", "hybrid", "copy"], default=None)
+    ap.add_argument("--cpu-oracle-table", action="store_true",
+                    help="time the CPU oracle on every workload (all cores and one core, whole "
+                         "workloads where that is feasible) and print a markdown table; no GPU work")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the 32K prefill (and the CPU oracle)")
     args = ap.parse_args()
@@ -767,6 +970,9 @@ def main():
               "measured workload", file=sys.stderr)
         sys.exit(2)
 
+    if args.cpu_oracle_table:
+        print_cpu_oracle_table()
+        return
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -817,7 +1023,8 @@ def main():
         workloads[name] = r
         note(f"hybrid {name}: {r['us']:.2f} us/call ({r['GB/s']:.0f} GB/s)")
     cpu = cpu_baseline()
-    note(f"cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads")
+    note(f"cpu oracle: {cpu['value'] * 1e3:.3f} GFLOP/s on {cpu['cores']} threads "
+         f"({cpu['cpu_model']}, nproc {cpu['nproc']})")
     from block_sparse_streaming_amd import inputs
     line = {
         "metric": METRIC,

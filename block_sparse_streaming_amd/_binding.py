@@ -43,14 +43,16 @@ _lib = None
 
 
 def load_library() -> ctypes.CDLL:
-    """Load libssa.so (built in-tree by ``__graft_entry__.build()``)."""
+    """Load libssa.so (built in-tree by ``__graft_entry__.build()``), or the
+    build SSA_LIB names (the host-sanitized build of tests/sanitize.py)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+    path = os.environ.get("SSA_LIB") or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
                            "(hipcc --offload-arch=gfx950); there is no fallback path")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     p, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                             ctypes.c_size_t)
     i64p = ctypes.POINTER(ctypes.c_int64)

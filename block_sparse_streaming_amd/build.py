@@ -71,5 +71,33 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SANITIZE_DIR = os.path.join(BUILD_DIR, "sanitize")
+SANITIZED_LIB = os.path.join(SANITIZE_DIR, "libssa_host_asan.so")
+
+
+def build_host_sanitized() -> str:
+    """A second libssa.so whose host code (api.cpp: argument checks, planning,
+    workspace layout) is built with AddressSanitizer and UBSan; the kernels
+    are the normal objects (device code is not sanitized). Loaded only when
+    SSA_LIB names it, with the clang ASan runtime preloaded."""
+    if not all(os.path.exists(os.path.join(BUILD_DIR, os.path.splitext(x)[0] + ".o")) for x in SOURCES):
+        build()
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    cc = hipcc()
+    obj = os.path.join(SANITIZE_DIR, "api.o")
+    host_flags = []
+    for f in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+              "-fno-omit-frame-pointer", "-g"):
+        host_flags += ["-Xarch_host", f]
+    subprocess.check_call([cc, *common_flags(), *host_flags, "-x", "hip", "-c",
+                           os.path.join(CSRC, "api.cpp"), "-o", obj],
+                          stderr=subprocess.DEVNULL)
+    objs = [obj] + [os.path.join(BUILD_DIR, os.path.splitext(x)[0] + ".o") for x in SOURCES if x != "api.cpp"]
+    tmp = SANITIZED_LIB + ".tmp"
+    subprocess.check_call([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -54,7 +54,16 @@
 extern "C" {
 #endif
 
-typedef enum ssa_status {
+/* The enums are int-sized in C and C++ alike. In C++ they get int as their
+ * fixed underlying type, so any int a C caller passes is a value of the type
+ * (an unknown dtype is then rejected, not undefined behaviour). */
+#ifdef __cplusplus
+#define SSA_ENUM_BASE : int
+#else
+#define SSA_ENUM_BASE
+#endif
+
+typedef enum ssa_status SSA_ENUM_BASE {
     SSA_OK = 0,
     SSA_ERR_INVALID_ARG = 1,
     SSA_ERR_UNSUPPORTED = 2,
@@ -63,7 +72,7 @@ typedef enum ssa_status {
 } ssa_status;
 
 /* Element type of q, k, v, caches and outputs (lse is always fp32). */
-typedef enum ssa_dtype { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
+typedef enum ssa_dtype SSA_ENUM_BASE { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
 
 /* The SSA pattern: block size b >= 1, sink blocks s >= 0, local blocks l >= 1
  * (the local blocks include the query's own block, so l >= 1 keeps every row

@@ -26,28 +26,37 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssa_oracle.c")
 _LIB = os.path.join(_HERE, "libssa_oracle.so")
+# The same source built with AddressSanitizer and UBSan (tests/sanitize.py);
+# SSA_ORACLE_LIB names the build to load.
+_LIB_SANITIZED = os.path.join(_HERE, "libssa_oracle_asan.so")
 _lib = None
 
 ELEM_F32 = 0
 ELEM_BF16 = 1
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, no hand vectorisation)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no hand vectorisation); with
+    sanitize, a separate AddressSanitizer + UBSan build (-O1, aborting on the
+    first report), loaded only when SSA_ORACLE_LIB names it."""
+    out = _LIB_SANITIZED if sanitize else _LIB
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        tmp = out + ".tmp"
+        flags = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"])
+        subprocess.check_call(["gcc", *flags, "-fopenmp", "-shared", "-fPIC", "-std=c11",
                                "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("SSA_ORACLE_LIB") or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         p, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.oracle_ssa_prefill.restype = i32
         lib.oracle_ssa_prefill.argtypes = [i32, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
