@@ -723,23 +723,31 @@ _ORACLE_THREADS = []   # the oracle's thread count before any change (all cores)
 
 
 def _oracle_seconds(threads: int, fn) -> float:
-    """Seconds of fn() with the oracle on `threads` threads (0: all)."""
+    """Seconds of fn() with the oracle on `threads` threads (0: all). fn may
+    be a list of callables (pieces of one workload): their times add up, and
+    a progress line goes to stderr after each."""
     import oracle
     if not _ORACLE_THREADS:
         _ORACLE_THREADS.append(oracle.max_threads())
     oracle.set_threads(threads if threads > 0 else _ORACLE_THREADS[0])
     try:
-        t0 = time.perf_counter()
-        fn()
-        return time.perf_counter() - t0
+        total = 0.0
+        for f in (fn if isinstance(fn, list) else [fn]):
+            t0 = time.perf_counter()
+            f()
+            total += time.perf_counter() - t0
+            print(f"# oracle: {total:.1f} s on {threads or _ORACLE_THREADS[0]} thread(s)", file=sys.stderr,
+                  flush=True)
+        return total
     finally:
         oracle.set_threads(_ORACLE_THREADS[0])
 
 
-def _prefill_oracle(cfg, heads: int, rows, gen):
+def _prefill_oracle(cfg, heads: int, rows, gen, pieces: int = 1):
     """A callable running the oracle on `rows` of `heads` query heads of the
     workload's shape (inputs drawn on the CPU, same distribution and dtype),
-    and the attended (query, key) pairs it evaluates."""
+    and the attended (query, key) pairs it evaluates. With pieces > 1, a list
+    of callables over consecutive parts of the rows (one set of inputs)."""
     import oracle
     from block_sparse_streaming_amd import inputs
     q = _bits(_cpu_randn((cfg.B, cfg.N, heads, cfg.d_qk), cfg.dtype, gen))
@@ -750,7 +758,10 @@ def _prefill_oracle(cfg, heads: int, rows, gen):
     r = np.arange(cfg.N) if rows is None else np.asarray(rows)
     lo = np.maximum(s * b, (r // b - l + 1) * b)
     pairs = int((np.minimum(s * b, r + 1) + np.maximum(0, r + 1 - lo)).sum()) * heads * cfg.B
-    return (lambda: oracle.prefill(q, k, v, **pat, scale=cfg.scale, rows=rows)), pairs
+    if pieces == 1:
+        return (lambda: oracle.prefill(q, k, v, **pat, scale=cfg.scale, rows=rows)), pairs
+    parts = np.array_split(r, pieces)
+    return [(lambda p=p: oracle.prefill(q, k, v, **pat, scale=cfg.scale, rows=p)) for p in parts], pairs
 
 
 def _decode_oracle(cfg, lens, full: bool, gen):
@@ -834,7 +845,8 @@ def cpu_baseline(full_runs: bool = False):
     fn_all, pairs = _prefill_oracle(cfg, cfg.Hq, None, gen)
     t_all = _oracle_seconds(0, fn_all)
     if full_runs:
-        t_one, scale_one, sample = _oracle_seconds(1, fn_all), 1.0, "whole workload"
+        parts, _ = _prefill_oracle(cfg, cfg.Hq, None, gen, pieces=16)   # progress lines
+        t_one, scale_one, sample = _oracle_seconds(1, parts), 1.0, "whole workload"
     else:
         rows = np.concatenate([np.arange(t * 128, t * 128 + 128) for t in range(0, cfg.N // 128, 16)])
         fn1, pairs1 = _prefill_oracle(cfg, cfg.Hq, rows, gen)
@@ -869,7 +881,8 @@ def cpu_baseline(full_runs: bool = False):
         "ssa_decode", "whole workload", 1.0, _oracle_seconds(0, fn), _oracle_seconds(1, fn), nbytes,
         "GB/s", 1e-9, threads)
     sub = lens if full_runs else lens[:1]
-    fn, toks_s = _decode_oracle(cfg, sub, True, gen)
+    pieces = [_decode_oracle(cfg, sub[k:k + 2], True, gen) for k in range(0, len(sub), 2)]
+    fn, toks_s = [p[0] for p in pieces], sum(p[1] for p in pieces)
     toks_full = sum(lens)
     table[cfg.name + ":full_attn_decode"] = _entry(
         "full_attn_decode", "whole workload" if full_runs else
