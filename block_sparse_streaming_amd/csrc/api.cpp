@@ -49,8 +49,8 @@ bool dtype_ok(ssa_dtype t) { return t == SSA_F32 || t == SSA_BF16; }
 
 // The latent split kernel holds a whole CU (its ring of latent rows fills the
 // LDS): once a call has this many work-groups, wider splits cost no
-// parallelism and cut the fp32 partials each split writes and the merge
-// reads (64 heads x 512 x 4 B per split, about the size of 128 latent rows).
+// parallelism and cut the bf16 partials each split writes and the merge
+// reads (64 heads x 512 x 2 B per split, about the size of 57 latent rows).
 constexpr int64_t kLatentTargetWgs = 256;
 
 // Work plan of a decode call; false if no compiled kernel fits the shape.
