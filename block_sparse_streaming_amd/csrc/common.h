@@ -104,6 +104,29 @@ __device__ __forceinline__ void dma16_untracked(const void *src, uint32_t lds_wa
         : "memory");
 }
 
+// The same untracked 16-byte transfer addressed as a wave-uniform base plus a
+// 32-bit per-lane byte offset (the global instruction's scalar-base form):
+// no 64-bit address arithmetic per lane and per transfer. `base` must be
+// uniform; it is read from the first active lane.
+__device__ __forceinline__ void dma16_sbase_untracked(const void *base, uint32_t off, uint32_t lds_wave_base) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    // readfirstlane returns a signed int: take both halves as uint32_t before
+    // widening, or a low half with bit 31 set would sign-extend over the high one.
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t sb = ((uint64_t)hi << 32) | lo;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(sb), "s"(lds_wave_base)
+        : "memory");
+}
+
 // A 4-byte untracked global -> LDS transfer: lane i's dword lands at
 // lds_wave_base + 4 i. Same contract as dma16_untracked.
 __device__ __forceinline__ void dma4_untracked(const void *src, uint32_t lds_wave_base) {

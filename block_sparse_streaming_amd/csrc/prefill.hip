@@ -115,8 +115,13 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         qt = wg % a.num_qtiles;
         hb = wg / a.num_qtiles;
     }
-    const int h = hb % a.Hq, bb = hb / a.Hq;
-    const int g = h / a.group;
+    // The divisions above run on the vector unit; taking their (uniform)
+    // results back to scalar registers keeps every base address derived from
+    // them scalar, which the scalar-base transfers below need.
+    qt = __builtin_amdgcn_readfirstlane(qt);
+    hb = __builtin_amdgcn_readfirstlane(hb);
+    const int h = __builtin_amdgcn_readfirstlane(hb % a.Hq), bb = __builtin_amdgcn_readfirstlane(hb / a.Hq);
+    const int g = __builtin_amdgcn_readfirstlane(h / a.group);
 
     // Sequence geometry. Paged: the chunk's rows [0, q_len) sit at positions
     // pos0 .. pos0 + q_len - 1 of a context of ctx tokens; row r of the chunk
@@ -183,6 +188,13 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
     auto dma = [&](const void *src, uint16_t *dst) __attribute__((always_inline)) {
         if constexpr (kTrackedDma) dma16(src, dst);
         else dma16_untracked(src, lds_addr(dst));
+    };
+    // A transfer from a wave-uniform base plus a per-lane byte offset (rows of
+    // one contiguous range, or of one page). The dual kernel keeps the 64-bit
+    // form: the scalar bases cost it registers it does not have.
+    auto dma_at = [&](const char *base, uint32_t off, uint16_t *dst) __attribute__((always_inline)) {
+        if constexpr (kTrackedDma || DUAL) dma(base + off, dst);
+        else dma16_sbase_untracked(base, off, lds_addr(dst));
     };
     auto load_q = [&]() __attribute__((always_inline)) {
         const uint16_t *qrow = qbase + row_idx * a.qs[1] + 8 * hi;
@@ -269,9 +281,9 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             const char *kt = (const char *)(kbase + pg0 * a.ks[0] + (int64_t)sl0 * a.ks[1]);
             const char *vt = (const char *)(vbase + pg0 * a.vs[0] + (int64_t)sl0 * a.vs[1]);
 #pragma unroll
-            for (int n = 0; n < NIK; ++n) dma(kt + koff[n], kb + (wave * NIK + n) * 512);
+            for (int n = 0; n < NIK; ++n) dma_at(kt, koff[n], kb + (wave * NIK + n) * 512);
 #pragma unroll
-            for (int n = 0; n < NIV; ++n) dma(vt + voff[n], vb + (wave * NIV + n) * 512);
+            for (int n = 0; n < NIV; ++n) dma_at(vt, voff[n], vb + (wave * NIV + n) * 512);
             return;
         }
         auto src = [&](int p, int C, int swz, int64_t s0, int64_t s1) __attribute__((always_inline)) {
@@ -301,19 +313,19 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
         const char *vt = (const char *)(vbase + (int64_t)st.j0 * a.vs[1]);
         if (kKeepOffsets && rows_valid >= kBN) {
 #pragma unroll
-            for (int n = 0; n < NIK; ++n) dma(kt + koff[n], kb + (wave * NIK + n) * 512);
+            for (int n = 0; n < NIK; ++n) dma_at(kt, koff[n], kb + (wave * NIK + n) * 512);
 #pragma unroll
-            for (int n = 0; n < NIV; ++n) dma(vt + voff[n], vb + (wave * NIV + n) * 512);
+            for (int n = 0; n < NIV; ++n) dma_at(vt, voff[n], vb + (wave * NIV + n) * 512);
         } else {
 #pragma unroll
             for (int n = 0; n < NIK; ++n) {
                 const int p = (wave * NIK + n) * 64 + lane;
-                dma(kt + dma_off(p, CK, k_swz<CK>(p / CK), ks1, rows_valid), kb + (wave * NIK + n) * 512);
+                dma_at(kt, dma_off(p, CK, k_swz<CK>(p / CK), ks1, rows_valid), kb + (wave * NIK + n) * 512);
             }
 #pragma unroll
             for (int n = 0; n < NIV; ++n) {
                 const int p = (wave * NIV + n) * 64 + lane;
-                dma(vt + dma_off(p, CV, v_swz<CV>(p / CV), vs1, rows_valid), vb + (wave * NIV + n) * 512);
+                dma_at(vt, dma_off(p, CV, v_swz<CV>(p / CV), vs1, rows_valid), vb + (wave * NIV + n) * 512);
             }
         }
     };
