@@ -530,6 +530,43 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             lse_out[li] = (m_run + log2f(l_tot)) * kLn2;
         }
     };
+    // The final output of the single-result modes, staged through LDS (the
+    // V buffers, free once every wave has passed the barrier below): each
+    // wave writes its 32 x DV tile row-major (16-byte units XOR-swizzled by
+    // row), then reads it back as whole rows, so that every global store
+    // writes 16 contiguous bytes and a store instruction covers whole rows
+    // instead of 8-byte pieces of 32 rows.
+    auto store_out_staged = [&]() __attribute__((always_inline)) {
+        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        const float inv = 1.f / l_tot;
+        constexpr int kRowB = DV * 2, kUnits = kRowB / 16;
+        static_assert(kUnits == 8 || kUnits == 16, "rows of 128 or 256 bytes");
+        barrier_lds_drained();
+        char *stage = (char *)(wave < 2 ? v_buf0 : v_buf1) + (wave & 1) * 32 * kRowB;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const u32x2 w{pack_bf16x2(oacc[d][4 * rq] * inv, oacc[d][4 * rq + 1] * inv),
+                              pack_bf16x2(oacc[d][4 * rq + 2] * inv, oacc[d][4 * rq + 3] * inv)};
+                const int unit = (4 * d + rq) ^ (l32 & (kUnits - 1));
+                *(u32x2 *)(stage + l32 * kRowB + unit * 16 + 8 * hi) = w;
+            }
+        const int r_base = tr.q0 + wave * 32;  // position of the wave's first row
+        const int64_t idx_base = PAGED ? (int64_t)q_start + (r_base - pos0) : (int64_t)r_base;
+        uint16_t *obase = (uint16_t *)a.o + bb * a.os[0] + h * a.os[2];
+#pragma unroll
+        for (int n = 0; n < 32 * kUnits / 64; ++n) {
+            const int lin = n * 64 + lane;
+            const int r = lin / kUnits, u = lin % kUnits;
+            const u32x4 v = *(const u32x4 *)(stage + r * kRowB + ((u ^ (r & (kUnits - 1))) * 16));
+            if (r_base + r < n_end) *(u32x4 *)(obase + (idx_base + r) * a.os[1] + u * 8) = v;
+        }
+        if (row_ok && a.lse && hi == 0) {
+            const int64_t li = PAGED ? row_idx * a.Hq + h : ((int64_t)bb * a.Hq + h) * a.N + i;
+            a.lse[li] = (m_run + log2f(l_tot)) * kLn2;
+        }
+    };
     auto step = [&](auto whole, int t, const uint16_t *kb, const uint16_t *vb) __attribute__((always_inline)) {
         compute(whole, t, kb, vb);
         // The SSA result. Copies without masks run past the SSA range only.
@@ -621,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
 
     // Epilogue: O = O / l, lse = ln 2 * (m + log2 l).
     if constexpr (!DUAL) {
-        store_out(a.o, a.lse);
+        store_out_staged();
     } else {
         store_out(a.o_full, a.lse_full);
         if (a.o_mix) {
