@@ -77,6 +77,16 @@ __device__ __forceinline__ int dual_swz(int row) {
 // a tile transfer fetches: tile row p / C at physical unit p % C, which holds
 // logical unit (p % C) ^ swz(row). Rows past rows_valid re-read the last valid
 // row; those rows are masked by the consumer.
+// A row transfer global -> LDS at base + off (base wave-uniform): the
+// scalar-base form at d_qk <= 128, where it saves the 64-bit address
+// arithmetic per transfer; at d_qk = 192 the per-lane 64-bit form measured
+// faster.
+template <int DQK>
+__device__ __forceinline__ void dma_at(const char *base, uint32_t off, uint32_t lds) {
+    if constexpr (DQK > 128) dma16_untracked(base + off, lds);
+    else dma16_sbase_untracked(base, off, lds);
+}
+
 template <int C>
 __device__ __forceinline__ uint32_t dma_off(int p, int stride, int rows_valid) {
     int row = p / C;
@@ -157,10 +167,12 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
     const int l32 = lane & 31, hi = lane >> 5;
 
     const int wg = xcd_remap(blockIdx.x, a.dq_wgs);
-    const int qt = wg % a.num_qtiles;
-    const int hb = wg / a.num_qtiles;
-    const int h = hb % a.Hq, bb = hb / a.Hq;
-    const int g = h / a.group;
+    // Tile indices back in scalar registers (the divisions run on the vector
+    // unit), so that the transfer bases derived from them stay scalar.
+    const int qt = __builtin_amdgcn_readfirstlane(wg % a.num_qtiles);
+    const int hb = __builtin_amdgcn_readfirstlane(wg / a.num_qtiles);
+    const int h = __builtin_amdgcn_readfirstlane(hb % a.Hq), bb = __builtin_amdgcn_readfirstlane(hb / a.Hq);
+    const int g = __builtin_amdgcn_readfirstlane(h / a.group);
 
     const TileRanges tr = tile_ranges(a, qt);
     const int i = tr.q0 + wave * 32 + l32;  // this lane's query row
@@ -243,12 +255,12 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
 #pragma unroll
         for (int n = 0; n < NIK; ++n) {
             const int p = (wave * NIK + n) * 64 + lane;
-            dma16_untracked(kt + dma_off<CK>(p, ks1, rows_valid), kb + (wave * NIK + n) * 1024);
+            dma_at<DQK>(kt, dma_off<CK>(p, ks1, rows_valid), kb + (wave * NIK + n) * 1024);
         }
 #pragma unroll
         for (int n = 0; n < NIV; ++n) {
             const int p = (wave * NIV + n) * 64 + lane;
-            dma16_untracked(vt + dma_off<CV>(p, vs1, rows_valid), vb + (wave * NIV + n) * 1024);
+            dma_at<DQK>(vt, dma_off<CV>(p, vs1, rows_valid), vb + (wave * NIV + n) * 1024);
         }
     };
 
@@ -479,6 +491,12 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
         r0 = kt * kBM;
         r1 = key_row_end(a, k1 - 1);
     }
+    kt = __builtin_amdgcn_readfirstlane(kt);
+    g = __builtin_amdgcn_readfirstlane(g);
+    bb = __builtin_amdgcn_readfirstlane(bb);
+    ch = __builtin_amdgcn_readfirstlane(ch);
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+    r1 = __builtin_amdgcn_readfirstlane(r1);
     const int nsub = r1 > r0 ? (r1 - r0 + KR - 1) / KR : 0;
     const int T = a.group * nsub;
     // Visit order at d_qk = 192 (key tiles past the sink): the query
@@ -558,12 +576,12 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
 #pragma unroll
         for (int n = 0; n < NIQ; ++n) {
             const int p = (wave * NIQ + n) * 64 + lane;
-            dma16_untracked(qt + dma_off<CQ>(p, qs1i, rows_valid), qb + (wave * NIQ + n) * 1024);
+            dma_at<DQK>(qt, dma_off<CQ>(p, qs1i, rows_valid), qb + (wave * NIQ + n) * 1024);
         }
 #pragma unroll
         for (int n = 0; n < NID; ++n) {
             const int p = (wave * NID + n) * 64 + lane;
-            dma16_untracked(dt + dma_off<CD>(p, ds1i, rows_valid), db + (wave * NID + n) * 1024);
+            dma_at<DQK>(dt, dma_off<CD>(p, ds1i, rows_valid), db + (wave * NID + n) * 1024);
         }
         // Row statistics of rows i0..i0+KR-1: NG * 512 contiguous bytes
         // (i0 is a multiple of 128, KR rows stay below n_pad), shared out.
