@@ -60,10 +60,35 @@ def decode_selected_tokens(L: int, block: int, sink: int, local: int) -> int:
     return min(sb, L) + max(0, L - lo)
 
 
+SETTLE_S = [0.5]   # seconds of untimed back-to-back calls before each timed region (--settle)
+
+
+def settle(fn, seconds: float) -> None:
+    """Run fn() back to back, untimed, for about `seconds` of wall-clock time.
+    After an idle or a lighter phase the GPU's clocks take tens of milliseconds
+    of sustained load to reach their steady state (the 32K prefill runs its
+    first ~30 launches at ~0.35 ms, then ~0.29 ms); a timed region that starts
+    earlier measures that ramp instead of the kernel."""
+    import torch
+    if seconds <= 0:
+        return
+    t0 = time.perf_counter()
+    n = 1
+    while True:
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+        n = min(2 * n, 64)
+
+
 def time_events(fn, iters: int) -> float:
     """Average milliseconds of fn() over iters back-to-back calls, by HIP events
-    on the current stream, synchronised before and after."""
+    on the current stream, synchronised before and after; the calls are timed
+    after settle(fn)."""
     import torch
+    settle(fn, SETTLE_S[0])
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -969,6 +994,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed back-to-back calls after the warmup steps, before each "
+                         "timed region (clock ramp); 0 disables")
     ap.add_argument("--profile", choices=["prefill", "prefill_fp32", "prefill_256k", "decode", "backward",
                                           "backward_256k", "dual", "extend", "hybrid", "copy"], default=None)
     ap.add_argument("--cpu-oracle-table", action="store_true",
@@ -977,6 +1005,7 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the 32K prefill (and the CPU oracle)")
     args = ap.parse_args()
+    SETTLE_S[0] = max(0.0, args.settle)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path "
               "shards by head or by sequence with no communication, so one GPU's share is the "
@@ -1046,6 +1075,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S[0],
         "ms_per_step": head["ms"],
         "higher_is_better": True,
         "scaling": "weak",
