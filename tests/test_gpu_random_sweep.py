@@ -1,6 +1,7 @@
-"""Seeded random sweep of prefill and backward shapes and patterns against the
-oracle: sequence lengths, batch, grouped heads, head dims, dtypes and
-(block, sink, local) drawn at random (fixed seed), so that combinations the
+"""Seeded random sweeps against the oracle: prefill and backward (sequence
+lengths, batch, grouped heads, head dims, dtypes, (block, sink, local)) and
+decode (MHA / GQA / latent heads, page sizes, context lengths from 0, SSA and
+full attention), drawn at random with fixed seeds, so that combinations the
 hand-picked cases do not list are also compared element by element."""
 import math
 
@@ -11,7 +12,7 @@ import torch
 import block_sparse_streaming_amd as ssa
 import oracle
 from block_sparse_streaming_amd import inputs
-from tests.gpu_util import assert_grad_parity, assert_lse, assert_parity, host, say
+from tests.gpu_util import assert_grad_parity, assert_lse, assert_parity, compact_paged, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +82,59 @@ def test_backward_random(case):
     rq, rk, rv = oracle.backward(host(q), host(k), host(v), host(do), **pattern, scale=scale)
     for got, ref, name in ((dq, rq, "dq"), (dk, rk, "dk"), (dvv, rv, "dv")):
         assert_grad_parity(got, ref, _ids(case) + " " + name)
+
+
+def _draw_decode(n_cases: int, seed: int):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n_cases):
+        latent = rng.random() < 0.3
+        if latent:
+            dtype, hkv, group, d_qk, d_v = torch.bfloat16, 1, int(rng.choice([16, 32, 64])), 576, 512
+        else:
+            dtype = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+            d = int(rng.choice([64, 128, 256]))
+            group = int(rng.choice([g for g in (1, 2, 4, 8) if g * d <= 1024 and not (g == 8 and d == 256)]))
+            hkv, d_qk, d_v = int(rng.integers(1, 3)), d, d
+        page = int(rng.choice([1, 16, 64, 128, 256]))
+        block = int(rng.choice([16, 64, 100, 128]))
+        sink = int(rng.integers(0, 3))
+        local = int(rng.integers(1, 9))
+        nseq = int(rng.integers(1, 5))
+        lens = tuple(int(x) for x in rng.integers(0, 6000, size=nseq))
+        full = bool(rng.random() < 0.3)
+        cases.append((dtype, hkv * group, hkv, d_qk, d_v, latent, page, (block, sink, local), lens, full,
+                      int(rng.integers(1 << 30))))
+    return cases
+
+
+DEC_CASES = _draw_decode(14, 20261204)
+
+
+def _dec_ids(c):
+    dtype, hq, hkv, dqk, dv, latent, page, (b, s, l), lens, full, _ = c
+    return (f"{str(dtype)[6:]}-H{hq}/{hkv}-d{dqk}/{dv}{'-latent' if latent else ''}-page{page}"
+            f"-b{b}s{s}l{l}-{len(lens)}seq{'-full' if full else ''}")
+
+
+@pytest.mark.parametrize("case", DEC_CASES, ids=_dec_ids)
+def test_decode_random(case):
+    dtype, hq, hkv, dqk, dv, latent, page, (b, s, l), lens, full, seed = case
+    cfg = inputs.DecodeConfig("random", dtype, hq, hkv, dqk, dv, latent, seed)
+    inp = inputs.decode_inputs(cfg, DEV, lens=lens, page_size=page, spare_pages=2)
+    pattern = dict(block=b, sink=s, local=l)
+    say("random decode", _dec_ids(case), lens)
+    if full:
+        o, lse = ssa.full_decode(inp.q, inp.k_cache, inp.v_cache, inp.page_table, inp.ctx_lens,
+                                 scale=cfg.scale, return_lse=True)
+    else:
+        o, lse = ssa.decode(inp.q, inp.k_cache, inp.v_cache, inp.page_table, inp.ctx_lens, **pattern,
+                            scale=cfg.scale, return_lse=True)
+    torch.cuda.synchronize()
+    kc, vc, table = compact_paged(inp.k_cache, inp.v_cache, inp.table_np, inp.lens, page, b, s, l, full,
+                                  latent_dv=dv if latent else None)
+    ro, rl = oracle.decode_paged(host(inp.q), kc, vc, table, np.array(inp.lens, np.int32),
+                                 **(dict(block=1, sink=0, local=1) if full else pattern),
+                                 scale=cfg.scale, full=full)
+    assert_parity(o, ro, dtype, _dec_ids(case))
+    assert_lse(lse, rl, dtype, _dec_ids(case))
