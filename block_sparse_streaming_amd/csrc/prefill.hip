@@ -694,23 +694,42 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
 // ---------------------------------------------------------------------------
 // fp32: register-staged kernel on the fp32 MFMA.
 // ---------------------------------------------------------------------------
-template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads, 2) void ssa_prefill_f32(const PrefillArgs a) {
-    constexpr int KSTR = DQK + 4, VSTR = DV + 4;  // padded rows (floats)
-    constexpr int NQ = DQK / 2, NDB = DV / 32;
-    __shared__ __attribute__((aligned(16))) float k_lds[kBN * KSTR];
-    __shared__ __attribute__((aligned(16))) float v_lds[kBN * VSTR];
+// One work-group = 32 query rows of one head, NW waves (8 at d = 64, 4 at
+// d = 128, as the LDS allows). All waves hold the same rows; wave w takes the
+// key sub-tiles t = w, w + NW, ... of the rows' key ranges and keeps its own
+// online-softmax state, and the states are merged through LDS at the end. Small fp32 workloads (2K tokens
+// x 4 heads) thus fill the chip with 4x the work-groups of 128-row tiles.
+// Each wave stages its sub-tile in a private LDS slice: K, then after the
+// scores V in the same slice (rows padded by 4 floats), so no barrier is
+// needed until the merge.
+constexpr int kF32Rows = 32;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int DQK, int DV>
+constexpr int f32_waves() { return DQK <= 64 ? 8 : 4; }
+
+template <int DQK, int DV>
+__global__ __launch_bounds__((64 * f32_waves<DQK, DV>()), 1) void ssa_prefill_f32(const PrefillArgs a) {
+    constexpr int NW = f32_waves<DQK, DV>();
+    constexpr int KSTR = DQK + 4, VSTR = DV + 4;  // padded rows (floats)
+    constexpr int SLICE = kBN * (KSTR > VSTR ? KSTR : VSTR);
+    constexpr int NQ = DQK / 2, NDB = DV / 32;
+    constexpr int OSTR = DV + 1;                    // merge rows, padded
+    static_assert(kF32Rows * OSTR + 2 * kF32Rows <= SLICE, "merge state fits a wave's slice");
+    __shared__ __attribute__((aligned(16))) float slices[NW][SLICE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
     const int wg = xcd_remap(blockIdx.x, a.total_wgs);
-    const int qt = wg % a.num_qtiles;
-    const int hb = wg / a.num_qtiles;
+    const int qt = __builtin_amdgcn_readfirstlane(wg % a.num_qtiles);
+    const int hb = __builtin_amdgcn_readfirstlane(wg / a.num_qtiles);
     const int h = hb % a.Hq, bb = hb / a.Hq;
     const int g = h / a.group;
 
-    const TileRanges tr = tile_ranges(a, qt);
-    const int i = tr.q0 + wave * 32 + l32;
+    const Geo geo = geo_of(a);
+    const int q0 = qt * kF32Rows;
+    const TileRanges tr = tile_ranges_at(geo, q0, imin(q0 + kF32Rows, a.N));
+    const int i = q0 + l32;
     const bool row_ok = i < a.N;
     const int lo_i = local_start(a, i);
 
@@ -732,33 +751,30 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_f32(const PrefillArgs
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
 
-    for (int t = 0; t < tr.n_total; ++t) {
-        const SubTile st = sub_tile(tr, t);
-        __syncthreads();
-        // Keys past the range end are zero-filled, never read.
-        constexpr int KCH = DQK / 4, VCH = DV / 4;
-        for (int c = tid; c < kBN * KCH; c += kThreads) {
-            const int row = c / KCH, col = c % KCH;
+    float *slice = slices[wave];
+    // Rows j0 .. j0 + 63 of a K or V matrix into the slice (rows past the
+    // range end zero-filled, never read from memory).
+    auto stage = [&](const float *base, int64_t stride, int D, int STR, const SubTile &st)
+        __attribute__((always_inline)) {
+        const int ch = D / 4;
+        for (int c = lane; c < kBN * ch; c += 64) {
+            const int row = c / ch, col = c % ch;
             const int j = st.j0 + row;
             f32x4 w = {0.f, 0.f, 0.f, 0.f};
-            if (j < st.re) w = *(const f32x4 *)(kbase + (int64_t)j * a.ks[1] + col * 4);
-            *(f32x4 *)(k_lds + row * KSTR + col * 4) = w;
+            if (j < st.re) w = *(const f32x4 *)(base + (int64_t)j * stride + col * 4);
+            *(f32x4 *)(slice + row * STR + col * 4) = w;
         }
-        for (int c = tid; c < kBN * VCH; c += kThreads) {
-            const int row = c / VCH, col = c % VCH;
-            const int j = st.j0 + row;
-            f32x4 w = {0.f, 0.f, 0.f, 0.f};
-            if (j < st.re) w = *(const f32x4 *)(vbase + (int64_t)j * a.vs[1] + col * 4);
-            *(f32x4 *)(v_lds + row * VSTR + col * 4) = w;
-        }
-        __syncthreads();
+    };
 
+    for (int t = wave; t < tr.n_total; t += NW) {
+        const SubTile st = sub_tile(tr, t);
+        stage(kbase, a.ks[1], DQK, KSTR, st);
         f32x16 sacc[2];
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kbk][r] = 0.f;
-            const float *krow = k_lds + (kbk * 32 + l32) * KSTR;
+            const float *krow = slice + (kbk * 32 + l32) * KSTR;
 #pragma unroll
             for (int ks = 0; ks < NQ; ++ks)
                 sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks + hi], qf[ks], sacc[kbk], 0, 0, 0);
@@ -796,6 +812,10 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_f32(const PrefillArgs
         for (int d = 0; d < NDB; ++d)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+        // V into the same slice, once every lane's K reads are done (LDS
+        // operations of a wave complete in order; the compiler keeps the
+        // order of these accesses to one array).
+        stage(vbase, a.vs[1], DV, VSTR, st);
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
@@ -803,25 +823,55 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_f32(const PrefillArgs
                 const int key = kbk * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
 #pragma unroll
                 for (int d = 0; d < NDB; ++d)
-                    oacc[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(v_lds[key * VSTR + d * 32 + l32], sacc[kbk][r],
+                    oacc[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(slice[key * VSTR + d * 32 + l32], sacc[kbk][r],
                                                                    oacc[d], 0, 0, 0);
             }
+        // The next sub-tile's K overwrites this V only after its products.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 
+    // Merge. Each wave leaves its unnormalised O (row l32, column c at
+    // slice[l32 * OSTR + c]) and its row max and sum; wave 0 combines them.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.f / l_tot;
-    if (row_ok) {
-        float *orow = (float *)a.o + bb * a.os[0] + (int64_t)i * a.os[1] + h * a.os[2];
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
+    for (int d = 0; d < NDB; ++d)
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int col = d * 32 + 8 * rq + 4 * hi;
-                *(f32x4 *)(orow + col) = f32x4{oacc[d][4 * rq] * inv, oacc[d][4 * rq + 1] * inv,
-                                               oacc[d][4 * rq + 2] * inv, oacc[d][4 * rq + 3] * inv};
-            }
-        if (a.lse && hi == 0) a.lse[((int64_t)bb * a.Hq + h) * a.N + i] = (m_run + log2f(l_tot)) * kLn2;
+        for (int r = 0; r < 16; ++r) slice[l32 * OSTR + d * 32 + 8 * (r >> 2) + 4 * hi + (r & 3)] = oacc[d][r];
+    if (hi == 0) {
+        slice[kF32Rows * OSTR + l32] = m_run;
+        slice[kF32Rows * OSTR + kF32Rows + l32] = l_tot;
     }
+    __syncthreads();
+    if (wave != 0) return;
+    float mw[NW], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        mw[w] = slices[w][kF32Rows * OSTR + l32];
+        M = fmaxf(M, mw[w]);
+    }
+    const float M_use = M == -INFINITY ? 0.f : M;
+    float ew[NW], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        ew[w] = fast_exp2(mw[w] - M_use);
+        L += ew[w] * slices[w][kF32Rows * OSTR + kF32Rows + l32];
+    }
+    if (!row_ok) return;
+    const float inv = 1.f / L;
+    float *orow = (float *)a.o + bb * a.os[0] + (int64_t)i * a.os[1] + h * a.os[2];
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            const int col = d * 32 + 8 * rq + 4 * hi;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += ew[w] * slices[w][l32 * OSTR + col + e];
+            *(f32x4 *)(orow + col) = v * inv;
+        }
+    if (a.lse && hi == 0) a.lse[((int64_t)bb * a.Hq + h) * a.N + i] = (M + log2f(L)) * kLn2;
 }
 
 template <typename K>
@@ -843,8 +893,19 @@ hipError_t launch_prefill(bool bf16, int d_qk, int d_v, const PrefillArgs &a, hi
         if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_bf16<128, 128, kModePlain>, a, stream);
         if (d_qk == 192 && d_v == 128) return launch(ssa_prefill_bf16<192, 128, kModePlain>, a, stream);
     } else {
-        if (d_qk == 64 && d_v == 64) return launch(ssa_prefill_f32<64, 64>, a, stream);
-        if (d_qk == 128 && d_v == 128) return launch(ssa_prefill_f32<128, 128>, a, stream);
+        // 32-row tiles (see ssa_prefill_f32).
+        PrefillArgs f = a;
+        f.num_qtiles = (a.N + kF32Rows - 1) / kF32Rows;
+        const int64_t wgs = (int64_t)f.num_qtiles * a.Hq * a.B;
+        if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+        f.total_wgs = (int32_t)wgs;
+        void *args[] = {(void *)&f};
+        if (d_qk == 64 && d_v == 64)
+            return hipLaunchKernel((const void *)ssa_prefill_f32<64, 64>, dim3(f.total_wgs),
+                                   dim3(64 * f32_waves<64, 64>()), args, 0, stream);
+        if (d_qk == 128 && d_v == 128)
+            return hipLaunchKernel((const void *)ssa_prefill_f32<128, 128>, dim3(f.total_wgs),
+                                   dim3(64 * f32_waves<128, 128>()), args, 0, stream);
     }
     return hipErrorInvalidValue;
 }
