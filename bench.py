@@ -210,7 +210,10 @@ def bench_prefill(cfg, steps: int, warmup: int):
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
     kernel = (f"ssa_prefill_bf16<{cfg.d_qk}, {cfg.d_v}, 0>" if bf16 else
               f"ssa_prefill_f32<{cfg.d_qk}, {cfg.d_v}>")
-    grid = -(-cfg.N // 128) * cfg.Hq * cfg.B * 256
+    if bf16:
+        grid = -(-cfg.N // 128) * cfg.Hq * cfg.B * 256      # 128-row tiles, 4 waves
+    else:
+        grid = -(-cfg.N // 32) * cfg.Hq * cfg.B * 64 * (8 if cfg.d_qk <= 64 else 4)   # 32-row tiles
     res = {"workload": cfg.name, "ms": ms, "steps": steps, "algorithmic_flops": flops,
            "TFLOP/s": tflops,
            "roofline": with_measured({"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
