@@ -827,7 +827,8 @@ __global__ __launch_bounds__((64 * f32_waves<DQK, DV>()), 1) void ssa_prefill_f3
                                                                    oacc[d], 0, 0, 0);
             }
         // The next sub-tile's K overwrites this V only after its products.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_lgkmcnt0();
+        asm volatile("" ::: "memory");
     }
 
     // Merge. Each wave leaves its unnormalised O (row l32, column c at
