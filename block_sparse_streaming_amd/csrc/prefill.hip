@@ -29,9 +29,14 @@
 //  * Work-group ids are remapped so that each XCD (own L2) runs a contiguous
 //    run of query tiles of one head: the sink tile and overlapping local tiles
 //    are then L2 hits.
+//  * Each transfer addresses a wave-uniform base in SGPRs plus a 32-bit lane
+//    offset computed once, so a transfer costs no vector address arithmetic.
+//  * The output tile is staged through LDS and written as whole 16-byte row
+//    pieces.
 //  * fp32 inputs take v_mfma_f32_32x32x2f32 (full fp32 products, no xf32) on a
-//    simpler register-staged loop; V then needs no transpose because each lane
-//    feeds one key per instruction.
+//    register-staged loop in which the waves of a 32-row work-group split the
+//    key sub-tiles and merge their softmax states; V then needs no transpose
+//    because each lane feeds one key per instruction.
 #include <type_traits>
 
 #include "common.h"
