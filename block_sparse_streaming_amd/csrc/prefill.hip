@@ -700,14 +700,17 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
 // fp32: register-staged kernel on the fp32 MFMA.
 // ---------------------------------------------------------------------------
 // One work-group = 32 query rows of one head, NW waves (8 at d = 64, 4 at
-// d = 128, as the LDS allows). All waves hold the same rows; wave w takes the
-// key sub-tiles t = w, w + NW, ... of the rows' key ranges and keeps its own
-// online-softmax state, and the states are merged through LDS at the end. Small fp32 workloads (2K tokens
-// x 4 heads) thus fill the chip with 4x the work-groups of 128-row tiles.
-// Each wave stages its sub-tile in a private LDS slice: K, then after the
-// scores V in the same slice (rows padded by 4 floats), so no barrier is
-// needed until the merge.
+// d = 128, as the LDS allows). All waves hold the same rows; the rows' key
+// ranges are cut into 32-key sub-tiles, wave w takes sub-tiles w, w + NW, ...
+// and keeps its own online-softmax state, and the states are merged through
+// LDS at the end. Small fp32 workloads (2K tokens x 4 heads) thus fill the
+// chip, and 32-key sub-tiles keep the waves' shares within one sub-tile of
+// each other. Each wave stages its sub-tile's K and V through a private LDS
+// slice (rows padded by 4 floats), so no barrier is needed until the merge;
+// the next sub-tile's rows are loaded into registers while this one is
+// computed.
 constexpr int kF32Rows = 32;
+constexpr int kF32Keys = 32;
 
 template <int DQK, int DV>
 constexpr int f32_waves() { return DQK <= 64 ? 8 : 4; }
@@ -716,8 +719,10 @@ template <int DQK, int DV>
 __global__ __launch_bounds__((64 * f32_waves<DQK, DV>()), 1) void ssa_prefill_f32(const PrefillArgs a) {
     constexpr int NW = f32_waves<DQK, DV>();
     constexpr int KSTR = DQK + 4, VSTR = DV + 4;  // padded rows (floats)
-    constexpr int SLICE = kBN * (KSTR > VSTR ? KSTR : VSTR);
+    constexpr int VOFF = kF32Keys * KSTR;          // V rows follow the K rows in a slice
+    constexpr int SLICE = kF32Keys * (KSTR + VSTR);
     constexpr int NQ = DQK / 2, NDB = DV / 32;
+    constexpr int NLK = kF32Keys * DQK / 4 / 64, NLV = kF32Keys * DV / 4 / 64;  // 16-byte loads per lane
     constexpr int OSTR = DV + 1;                    // merge rows, padded
     static_assert(kF32Rows * OSTR + 2 * kF32Rows <= SLICE, "merge state fits a wave's slice");
     __shared__ __attribute__((aligned(16))) float slices[NW][SLICE];
@@ -734,6 +739,22 @@ __global__ __launch_bounds__((64 * f32_waves<DQK, DV>()), 1) void ssa_prefill_f3
     const Geo geo = geo_of(a);
     const int q0 = qt * kF32Rows;
     const TileRanges tr = tile_ranges_at(geo, q0, imin(q0 + kF32Rows, a.N));
+    // 32-key sub-tiles of the two ranges.
+    const int n_sink = (tr.sink_end + kF32Keys - 1) / kF32Keys;
+    const int n_total = n_sink + (tr.q1 - tr.loc_begin + kF32Keys - 1) / kF32Keys;
+    struct Sub {
+        int j0, re;
+        bool need_mask;
+    };
+    auto sub_at = [&](int t) __attribute__((always_inline)) {
+        Sub st;
+        const bool local = t >= n_sink;
+        st.j0 = local ? tr.loc_begin + (t - n_sink) * kF32Keys : t * kF32Keys;
+        st.re = local ? tr.q1 : tr.sink_end;
+        st.need_mask = !((st.j0 + kF32Keys <= st.re) && (st.j0 + kF32Keys - 1 <= tr.q0) &&
+                         (!local || st.j0 >= tr.lo_last));
+        return st;
+    };
     const int i = q0 + l32;
     const bool row_ok = i < a.N;
     const int lo_i = local_start(a, i);
@@ -757,81 +778,91 @@ __global__ __launch_bounds__((64 * f32_waves<DQK, DV>()), 1) void ssa_prefill_f3
         for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
 
     float *slice = slices[wave];
-    // Rows j0 .. j0 + 63 of a K or V matrix into the slice (rows past the
-    // range end zero-filled, never read from memory).
-    auto stage = [&](const float *base, int64_t stride, int D, int STR, const SubTile &st)
-        __attribute__((always_inline)) {
-        const int ch = D / 4;
-        for (int c = lane; c < kBN * ch; c += 64) {
-            const int row = c / ch, col = c % ch;
+    // Rows j0 .. j0 + 31 of K and V in registers: load n covers row
+    // (lane + 64 n) / (D / 4), 16 bytes; rows past the range end are zero
+    // and never read from memory.
+    f32x4 kreg[NLK], vreg[NLV];
+    auto load_rows = [&](const Sub &st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < NLK; ++n) {
+            const int c = lane + 64 * n, row = c / (DQK / 4), col = c % (DQK / 4);
             const int j = st.j0 + row;
-            f32x4 w = {0.f, 0.f, 0.f, 0.f};
-            if (j < st.re) w = *(const f32x4 *)(base + (int64_t)j * stride + col * 4);
-            *(f32x4 *)(slice + row * STR + col * 4) = w;
+            kreg[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (j < st.re) kreg[n] = *(const f32x4 *)(kbase + (int64_t)j * a.ks[1] + col * 4);
+        }
+#pragma unroll
+        for (int n = 0; n < NLV; ++n) {
+            const int c = lane + 64 * n, row = c / (DV / 4), col = c % (DV / 4);
+            const int j = st.j0 + row;
+            vreg[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (j < st.re) vreg[n] = *(const f32x4 *)(vbase + (int64_t)j * a.vs[1] + col * 4);
+        }
+    };
+    auto store_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < NLK; ++n) {
+            const int c = lane + 64 * n, row = c / (DQK / 4), col = c % (DQK / 4);
+            *(f32x4 *)(slice + row * KSTR + col * 4) = kreg[n];
+        }
+#pragma unroll
+        for (int n = 0; n < NLV; ++n) {
+            const int c = lane + 64 * n, row = c / (DV / 4), col = c % (DV / 4);
+            *(f32x4 *)(slice + VOFF + row * VSTR + col * 4) = vreg[n];
         }
     };
 
-    for (int t = wave; t < tr.n_total; t += NW) {
-        const SubTile st = sub_tile(tr, t);
-        stage(kbase, a.ks[1], DQK, KSTR, st);
-        f32x16 sacc[2];
+    if (wave < n_total) load_rows(sub_at(wave));
+    for (int t = wave; t < n_total; t += NW) {
+        const Sub st = sub_at(t);
+        store_rows();
+        if (t + NW < n_total) load_rows(sub_at(t + NW));  // in flight during this sub-tile
+        f32x16 sacc;
 #pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk) {
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        const float *krow = slice + l32 * KSTR;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kbk][r] = 0.f;
-            const float *krow = slice + (kbk * 32 + l32) * KSTR;
-#pragma unroll
-            for (int ks = 0; ks < NQ; ++ks)
-                sacc[kbk] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks + hi], qf[ks], sacc[kbk], 0, 0, 0);
-        }
+        for (int ks = 0; ks < NQ; ++ks)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks + hi], qf[ks], sacc, 0, 0, 0);
         float mx = -INFINITY;
 #pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = sacc[kbk][r] * a.scale_log2;
-                if (st.need_mask) {
-                    const int j = st.j0 + kbk * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    const bool ok = (j < st.re) & (j <= i) & ((j < tr.sb) | (j >= lo_i));
-                    x = ok ? x : -INFINITY;
-                }
-                sacc[kbk][r] = x;
-                mx = fmaxf(mx, x);
+        for (int r = 0; r < 16; ++r) {
+            float x = sacc[r] * a.scale_log2;
+            if (st.need_mask) {
+                const int j = st.j0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                const bool ok = (j < st.re) & (j <= i) & ((j < tr.sb) | (j >= lo_i));
+                x = ok ? x : -INFINITY;
             }
+            sacc[r] = x;
+            mx = fmaxf(mx, x);
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = fast_exp2(m_run - m_use);
         float rs = 0.f;
 #pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(sacc[kbk][r] - m_use);
-                sacc[kbk][r] = p;
-                rs += p;
-            }
+        for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(sacc[r] - m_use);
+            sacc[r] = p;
+            rs += p;
+        }
         l_run = l_run * alpha + rs;
         m_run = m_new;
 #pragma unroll
         for (int d = 0; d < NDB; ++d)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-        // V into the same slice, once every lane's K reads are done (LDS
-        // operations of a wave complete in order; the compiler keeps the
-        // order of these accesses to one array).
-        stage(vbase, a.vs[1], DV, VSTR, st);
 #pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
+        for (int r = 0; r < 16; ++r) {
+            const int key = 8 * (r >> 2) + 4 * hi + (r & 3);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kbk * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-#pragma unroll
-                for (int d = 0; d < NDB; ++d)
-                    oacc[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(slice[key * VSTR + d * 32 + l32], sacc[kbk][r],
-                                                                   oacc[d], 0, 0, 0);
-            }
-        // The next sub-tile's K overwrites this V only after its products.
+            for (int d = 0; d < NDB; ++d)
+                oacc[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(slice[VOFF + key * VSTR + d * 32 + l32], sacc[r],
+                                                               oacc[d], 0, 0, 0);
+        }
+        // The next sub-tile's rows overwrite this slice only after these
+        // reads (LDS operations of a wave complete in order; the compiler
+        // keeps the order of accesses to one array).
         wait_lgkmcnt0();
         asm volatile("" ::: "memory");
     }
