@@ -630,6 +630,9 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
+    // Every wave is done with the ring buffers: wave w stages its 16 partial
+    // rows in buffer w below.
+    barrier_lds_drained();
     if (!active) return;
     // A split with no attended key (all of its listed tokens skipped) writes
     // o = 0 and lse = -inf, which the merge weights by zero.
@@ -637,11 +640,28 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     const int64_t slot = ((int64_t)bb * a.Hq + head) * a.plan.max_splits + split;
     // Partial outputs in bf16: per split they would otherwise weigh as much
     // as the split's latent rows (64 heads x 512 x 4 B against 128 x 1152 B).
-    uint16_t *wo = (uint16_t *)a.ws_o + slot * kLatDv + 4 * kg;
+    // They go out through LDS as whole 1 KB rows, one store instruction per
+    // head: written straight from the accumulators, each store instruction
+    // covered 8-byte pieces of 16 rows, and those scattered stores cost as
+    // much as a quarter of an SSA call. The staged rows' 16-byte units are
+    // XOR-swizzled by head so that the 16 heads of one write hit distinct
+    // banks.
+    char *stage = (char *)(wave == 0 ? c_b0 : wave == 1 ? c_b1 : wave == 2 ? c_b2 : c_b3);
+    static_assert(16 * kLatDv * 2 <= kLatCh * kLatDqk * 2, "a wave's partial rows fit one buffer");
+    constexpr int kRowB = kLatDv * 2;  // 1 KB
 #pragma unroll
-    for (int d = 0; d < kLatDv / 16; ++d)
-        *(u32x2 *)(wo + d * 16) = u32x2{pack_bf16x2(oacc[d][0] * inv, oacc[d][1] * inv),
-                                        pack_bf16x2(oacc[d][2] * inv, oacc[d][3] * inv)};
+    for (int d = 0; d < kLatDv / 16; ++d) {
+        const int unit = (2 * d + (kg >> 1)) ^ l16;
+        *(u32x2 *)(stage + l16 * kRowB + unit * 16 + 8 * (kg & 1)) =
+            u32x2{pack_bf16x2(oacc[d][0] * inv, oacc[d][1] * inv), pack_bf16x2(oacc[d][2] * inv, oacc[d][3] * inv)};
+    }
+    const int64_t slot0 = ((int64_t)bb * a.Hq + (head - l16)) * a.plan.max_splits + split;  // head l16 = 0
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const u32x4 v = *(const u32x4 *)(stage + r * kRowB + ((lane ^ r) * 16));
+        uint16_t *wrow = (uint16_t *)a.ws_o + (slot0 + (int64_t)r * a.plan.max_splits) * kLatDv;
+        *(u32x4 *)(wrow + lane * 8) = v;
+    }
     if (kg == 0) a.ws_lse[slot] = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
 }
 
