@@ -134,9 +134,22 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
 
     const int split = blockIdx.x, g = blockIdx.y, bb = blockIdx.z;
     const int tid = threadIdx.x, tg = tid / kTpt, tl = tid % kTpt;
+    // One split per row (a.plan.direct): the result goes straight to o and
+    // lse, as the merge would write it for a single split.
+    auto put_out = [&](int hh, int d, float v, float lse2) __attribute__((always_inline)) {
+        const int64_t row = (int64_t)bb * a.Hq + g * G + hh;
+        if constexpr (kBF16) ((uint16_t *)a.o)[row * D + d] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
+        else ((float *)a.o)[row * D + d] = v;
+        if (d == 0 && a.lse) a.lse[row] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
+    };
     // A split slot past the row's splits holds lse = -inf, so the merge needs
-    // neither the context length nor the split count.
+    // neither the context length nor the split count. Written directly, a row
+    // with no attended key has o = 0 and lse = -inf.
     auto no_split = [&]() __attribute__((always_inline)) {
+        if (a.plan.direct) {
+            for (int t = tid; t < G * D; t += kValuThreads) put_out(t / D, t % D, 0.f, -INFINITY);
+            return;
+        }
         for (int hh = tid; hh < G; hh += kValuThreads)
             a.ws_lse[((int64_t)bb * a.Hq + g * G + hh) * a.plan.max_splits + split] = -INFINITY;
     };
@@ -305,11 +318,16 @@ __global__ __launch_bounds__(kValuThreads) void decode_split_valu(const DecodeAr
             Z += w * sm_l[q][hh];
             O += w * sm_o[q][hh][d];
         }
-        const int64_t slot = ((int64_t)bb * a.Hq + g * G + hh) * a.plan.max_splits + split;
         // A split with no attended key (all of its listed tokens skipped):
         // o = 0 and lse = -inf, which the merge weights by zero.
-        a.ws_o[slot * D + d] = Z > 0.f ? O / Z : 0.f;
-        if (d == 0) a.ws_lse[slot] = Z > 0.f ? M + log2f(Z) : -INFINITY;
+        const float ov = Z > 0.f ? O / Z : 0.f, lse2 = Z > 0.f ? M + log2f(Z) : -INFINITY;
+        if (a.plan.direct) {
+            put_out(hh, d, ov, lse2);
+            continue;
+        }
+        const int64_t slot = ((int64_t)bb * a.Hq + g * G + hh) * a.plan.max_splits + split;
+        a.ws_o[slot * D + d] = ov;
+        if (d == 0) a.ws_lse[slot] = lse2;
     }
 }
 
@@ -405,30 +423,29 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     const int64_t t2 = sel.r2_begin + (s2 - sel.r1_end);                  // first token of part 2
     const int64_t lp2 = t2 / P;
     const int n2 = p_end > s2 ? (int)((sel.r2_begin + (p_end - sel.r1_end) - 1) / P - lp2 + 1) : 0;
+    const bool active = wave * 16 < heads_here;
+    const int head = g * a.group + hc * 64 + wave * 16 + l16;  // this lane's query head
+
+    // q^T operand (16 heads x 576 per wave) in registers. Every wave loads
+    // (one past the heads here loads wave 0's rows and never uses them), with
+    // no branch, and the loads go out before the page-id loads so that the
+    // two round trips overlap; both are complete before any transfer, so the
+    // transfer waits below count transfers only.
+    bf16x8 qf[kLatDqk / 32];
+    {
+        const int qhead = active ? head : head - wave * 16;
+        const uint16_t *qp = (const uint16_t *)a.q + ((int64_t)bb * a.Hq + qhead) * kLatDqk + 8 * kg;
+#pragma unroll
+        for (int ks = 0; ks < kLatDqk / 32; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + ks * 32));
+    }
     const int64_t seq = row_sequence(a, bb);
     if (!listed)
         for (int t = tid; t < n1 + n2; t += kLatThreads)
             pids[t] = a.page_table[seq * a.max_pages + (t < n1 ? lp1 + t : lp2 + (t - n1))];
-
-    const bool active = wave * 16 < heads_here;
-    const int head = g * a.group + hc * 64 + wave * 16 + l16;  // this lane's query head
-
-    // q^T operand (16 heads x 576 per wave) in registers, loaded before any
-    // transfer so that the transfer waits below count transfers only.
-    bf16x8 qf[kLatDqk / 32];
-    {
-        const uint16_t *qp = (const uint16_t *)a.q + ((int64_t)bb * a.Hq + head) * kLatDqk + 8 * kg;
+    // q is only ever an MFMA source operand, which may sit in AGPRs: park it
+    // there so the VGPRs hold the output accumulators and the scores.
 #pragma unroll
-        for (int ks = 0; ks < kLatDqk / 32; ++ks) {
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (active) w = *(const u32x4 *)(qp + ks * 32);
-            qf[ks] = __builtin_bit_cast(bf16x8, w);
-        }
-        // q is only ever an MFMA source operand, which may sit in AGPRs: park
-        // it there so the VGPRs hold the output accumulators and the scores.
-#pragma unroll
-        for (int ks = 0; ks < kLatDqk / 32; ++ks) asm volatile("" : "+a"(qf[ks]));
-    }
+    for (int ks = 0; ks < kLatDqk / 32; ++ks) asm volatile("" : "+a"(qf[ks]));
     __syncthreads();
 
     const uint16_t *kc = (const uint16_t *)a.kc + g * a.ks[2];
@@ -854,7 +871,7 @@ hipError_t launch_decode(bool bf16, int d_qk, int d_v, const DecodeArgs &a, hipS
     } else {
         err = bf16 ? launch_valu_d<true>(d_qk, a, stream) : launch_valu_d<false>(d_qk, a, stream);
     }
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || a.plan.direct) return err;
     const void *merge;
     switch (d_v) {
         case 64: merge = bf16 ? (const void *)decode_merge<true, 64> : (const void *)decode_merge<false, 64>; break;

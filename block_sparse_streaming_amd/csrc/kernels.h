@@ -84,6 +84,8 @@ struct DecodePlan {
     int split_tokens;  // attended tokens per split (multiple of the chunk size)
     int max_splits;    // splits per (sequence, head) the workspace holds
     int head_chunks;   // latent kernel: work-groups per kv head (64 heads each)
+    int direct;        // VALU kernel with one split and no list: the split kernel
+                       // writes o and lse itself and no merge runs
 };
 
 struct DecodeArgs {

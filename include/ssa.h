@@ -214,6 +214,10 @@ size_t ssa_prefill_backward_workspace_size(ssa_dtype dtype, int32_t batch, int32
  *   workspace  device scratch of at least ssa_decode_workspace_size(...)
  *              bytes (same shape arguments, full = 0); no initial contents
  *              are required. Calls sharing one workspace must not overlap.
+ *              A non-latent call whose attended tokens fit one split (a
+ *              window of at most 128 tokens; for full_attn_decode a table of
+ *              at most 256) writes o and lse from the split kernel and
+ *              leaves the workspace untouched; it is still checked.
  * Compiled: bf16 or fp32 with d_qk = d_v in {64, 128, 256} and
  * heads_q / heads_kv in {1, 2, 4, 8}, except group 8 at d = 256
  * (SSA_ERR_UNSUPPORTED); bf16 latent shape d_qk = 576, d_v = 512 with

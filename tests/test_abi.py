@@ -107,6 +107,11 @@ def test_decode_noalloc_validation():
     # 200 sequences x 64 heads, d = 128: 8 splits of fp32 partials, 52 MB
     assert ssa.decode_workspace_size(torch.bfloat16, 200, 64, 64, 128, 128, 128, 8) > 32 << 20
     assert noalloc_call(B=200, Hq=64, Hkv=64) == WORKSPACE
+    # 8,192-token window, 2 kv heads: 64 splits, 105 MB
+    big = dict(B=200, Hq=16, Hkv=2, max_pages=64, pattern=(128, 1, 63))
+    assert ssa.decode_workspace_size(torch.bfloat16, 200, 16, 2, 128, 128, 128, 64, block=128, sink=1,
+                                     local=63) > 32 << 20
+    assert noalloc_call(**big) == WORKSPACE
 
 
 @pytest.mark.parametrize("full", [False, True])

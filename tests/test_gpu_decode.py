@@ -145,6 +145,30 @@ def test_ragged_full_size():
     _check(cfg, inp, PAT, what=cfg.name)
 
 
+@pytest.mark.parametrize("dtype,group,page_size,pattern,full", [
+    (torch.bfloat16, 1, 128, PAT, False),
+    (torch.float32, 1, 16, dict(block=64, sink=1, local=1), False),      # 128-token window: one split
+    (torch.bfloat16, 4, 64, dict(block=32, sink=2, local=2), False),     # 128-token window: one split
+    (torch.bfloat16, 8, 128, dict(block=16, sink=1, local=3), False),    # 64-token window: one split
+    (torch.bfloat16, 2, 16, PAT, True),                                   # full, 256-token table: one split
+])
+def test_many_rows(dtype, group, page_size, pattern, full):
+    """Calls with hundreds of (sequence, kv head) rows and lengths from 0 up,
+    GQA groups, page sizes, fp32 and bf16; the windows of at most 128 tokens
+    (and the full decode over a 256-token table) fit one split, whose result
+    the split kernel writes without a merge."""
+    hkv = 16 if group == 1 else 8
+    B = -(-560 // hkv)
+    rng = np.random.default_rng(300 + group)
+    top = 256 if full else 3000
+    lens = [0, 1, 127, 128, 129, 255, 256] + [int(x) for x in rng.integers(0, top + 1, B - 7)]
+    lens = [min(x, top) for x in lens]
+    cfg = _cfg(dtype, hkv * group, hkv, 128, 128, seed=31 + group)
+    inp = inputs.decode_inputs(cfg, DEV, lens=tuple(lens), spare_pages=2, page_size=page_size)
+    _check(cfg, inp, pattern, full, what=f"many rows {dtype} G{group} page{page_size} {pattern} full={full}",
+           page_size=page_size)
+
+
 def test_page_order_and_poison_invariance():
     """Two physical page orders give bit-identical output; NaN in every page
     slot outside the window leaves the output finite and bit-identical."""
