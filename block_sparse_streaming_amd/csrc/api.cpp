@@ -199,6 +199,8 @@ ssa_status decode_common(ssa_dtype dtype, const void *q, const void *k_cache, co
                    topk_k))
         return SSA_ERR_UNSUPPORTED;
     if (topk_k > 0 && !add_list_splits(&plan, topk_k)) return SSA_ERR_UNSUPPORTED;
+    if (topk_k > 0 && plan.kind == ssa::kDecodeLatent && plan.split_tokens > ssa::kDecodeLatentMaxListSplit)
+        return SSA_ERR_UNSUPPORTED;  // the planner keeps latent splits within 1,024 tokens
     if (plan.kind == ssa::kDecodeLatent) {
         // The latent kernel reads the value as the first d_v entries of the key row.
         if (v_cache != k_cache || v_strides[0] != k_strides[0] || v_strides[1] != k_strides[1] ||

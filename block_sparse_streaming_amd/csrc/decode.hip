@@ -373,7 +373,10 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     __shared__ __attribute__((aligned(1024))) uint16_t c_b3[kLatCh * kLatDqk];
     __shared__ int32_t pids[kLatMaxPages];
     __shared__ int64_t rowtab[4][kLatRowsPerWave];
-    __shared__ uint32_t vmask[kLatBufs];  // listed tokens: attended rows of each ring slot
+    // A split of listed tokens: each position's row offset (relative to kc)
+    // and, one bit per position, whether it is attended.
+    __shared__ int64_t lrows[kDecodeLatentMaxListSplit];
+    __shared__ uint32_t lok[kDecodeLatentMaxListSplit / 32];
 
     // Work-groups of one XCD (own L2) take whole sequences, so the splits of a
     // sequence share q in that L2.
@@ -439,9 +442,39 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
         for (int ks = 0; ks < kLatDqk / 32; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + ks * 32));
     }
     const int64_t seq = row_sequence(a, bb);
-    if (!listed)
+    const uint32_t up_end = (uint32_t)p_end, ur1 = (uint32_t)sel.r1_end, ur2 = (uint32_t)sel.r2_begin;
+    const uint32_t uP = (uint32_t)P;
+    if (!listed) {
         for (int t = tid; t < n1 + n2; t += kLatThreads)
             pids[t] = a.page_table[seq * a.max_pages + (t < n1 ? lp1 + t : lp2 + (t - n1))];
+    } else {
+        // Every listed position's row, found through the list and the page
+        // table, once for the whole split: two dependent loads here, beside
+        // the q loads, instead of two per chunk behind the transfers in
+        // flight (a wait on a plain load also waits for those). A token
+        // inside the window, past the context or negative (padding) is
+        // skipped: its key is masked and token 0's row stands in for it.
+        // Whole waves per pass, so that each ballot covers 64 positions.
+        const uint32_t uL = (uint32_t)L, ur2end = ur2 < uL ? ur2 : uL;
+        const int padded = (ntok + 63) & ~63;  // <= kDecodeLatentMaxListSplit (host check)
+        for (int p = tid; p < padded; p += kLatThreads) {
+            bool ok = false;
+            int64_t off = 0;
+            if (p < ntok) {
+                const int t0 = a.topk[seq * a.topk_k + p_begin + p];
+                ok = t0 >= (int)ur1 && (uint32_t)t0 < ur2end;
+                const uint32_t tok = ok ? (uint32_t)t0 : 0u;
+                const uint32_t lp = tok / uP;
+                off = (int64_t)a.page_table[seq * a.max_pages + lp] * a.ks[0] + (int64_t)(tok - lp * uP) * a.ks[1];
+            }
+            lrows[p] = off;
+            const uint64_t bits = __builtin_amdgcn_ballot_w64(ok);
+            if (lane == 0) {
+                lok[p >> 5] = (uint32_t)bits;
+                lok[(p >> 5) + 1] = (uint32_t)(bits >> 32);
+            }
+        }
+    }
     // q is only ever an MFMA source operand, which may sit in AGPRs: park it
     // there so the VGPRs hold the output accumulators and the scores.
 #pragma unroll
@@ -451,8 +484,7 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
     const uint16_t *kc = (const uint16_t *)a.kc + g * a.ks[2];
     // Element offset (relative to kc) of the latent row at split position pp,
     // clamped to the split. Positions and tokens fit in 32 bits.
-    const uint32_t up_end = (uint32_t)p_end, ur1 = (uint32_t)sel.r1_end, ur2 = (uint32_t)sel.r2_begin;
-    const uint32_t uP = (uint32_t)P, ulp1 = (uint32_t)lp1, ulp2 = (uint32_t)lp2;
+    const uint32_t ulp1 = (uint32_t)lp1, ulp2 = (uint32_t)lp2;
     auto row_off = [&](uint32_t pp) __attribute__((always_inline)) -> int64_t {
         pp = pp < up_end ? pp : up_end - 1;
         const uint32_t tok = pp < ur1 ? pp : ur2 + (pp - ur1);
@@ -460,33 +492,16 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
         const int idx = pp < ur1 ? (int)(lp - ulp1) : n1 + (int)(lp - ulp2);
         return (int64_t)pids[idx] * a.ks[0] + (int64_t)(tok - lp * uP) * a.ks[1];
     };
-    // A listed token: its row, found through the list and the page table. A
-    // token inside the window, past the context or negative (padding) is
-    // skipped: its key is masked and token 0's row stands in for it.
-    const uint32_t uL = (uint32_t)L, ur2end = ur2 < uL ? ur2 : uL;
-    auto list_row_off = [&](uint32_t pp, bool &ok) __attribute__((always_inline)) -> int64_t {
-        pp = pp < up_end ? pp : up_end - 1;
-        const int t0 = a.topk[seq * a.topk_k + pp];
-        ok = t0 >= (int)ur1 && (uint32_t)t0 < ur2end;
-        const uint32_t tok = ok ? (uint32_t)t0 : 0u;
-        const uint32_t lp = tok / uP;
-        return (int64_t)a.page_table[seq * a.max_pages + lp] * a.ks[0] + (int64_t)(tok - lp * uP) * a.ks[1];
-    };
     // Transfers of chunk c: wave w moves rows 8w..8w+7. Lane slot p = 64n + lane
     // of its transfer n is row 8w + p / 72 at physical unit p % 72, which holds
     // logical unit (p % 72) ^ lat_swz(row). The wave's eight row offsets are
     // computed once by lanes 0..7 into rowtab (rows past the split's end
-    // repeat its last row). For listed tokens, byte w of vmask[c % 4] says
-    // which of the wave's eight rows are attended.
+    // repeat its last row); a listed split takes them from lrows.
     auto issue = [&](int c, uint16_t *buf) __attribute__((always_inline)) {
-        const uint32_t pp = (uint32_t)p_begin + (uint32_t)(c * kLatCh + wave * kLatRowsPerWave + lane);
-        if (!listed) {
-            if (lane < kLatRowsPerWave) rowtab[wave][lane] = row_off(pp);
-        } else {
-            bool ok = false;
-            if (lane < kLatRowsPerWave) rowtab[wave][lane] = list_row_off(pp, ok);
-            const uint64_t bits = __builtin_amdgcn_ballot_w64(ok && lane < kLatRowsPerWave);
-            if (lane == 0) ((uint8_t *)&vmask[c % kLatBufs])[wave] = (uint8_t)bits;
+        const int rel = c * kLatCh + wave * kLatRowsPerWave + lane;  // position in the split
+        if (lane < kLatRowsPerWave) {
+            if (!listed) rowtab[wave][lane] = row_off((uint32_t)p_begin + (uint32_t)rel);
+            else rowtab[wave][lane] = lrows[rel < ntok ? rel : ntok - 1];
         }
 #pragma unroll
         for (int n = 0; n < kLatDma; ++n) {
@@ -539,7 +554,7 @@ __global__ __launch_bounds__(kLatThreads, 1) void decode_split_latent(const Deco
             s[n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[n], qf[n >> 1], s[n & 1], 0, 0, 0);
         }
         const int nvalid = ntok - c * kLatCh;
-        const uint32_t vm = listed ? vmask[c % kLatBufs] : 0xffffffffu;
+        const uint32_t vm = listed ? lok[c] : 0xffffffffu;  // positions 32c .. 32c+31
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll

@@ -75,6 +75,9 @@ enum DecodeKind { kDecodeValu = 0, kDecodeLatent = 1 };
 // positions covers at most two token runs, so at most (T - 2) / page_size + 4
 // pages; the planner keeps that within this bound.
 constexpr int kDecodeLatentMaxPages = 256;
+// It also keeps the row offsets of a split of listed tokens (hybrid decode)
+// in LDS: at most this many positions per split.
+constexpr int kDecodeLatentMaxListSplit = 1024;
 
 // How a decode call is cut into work-groups. Computed on the host from shapes
 // only (context lengths live on the device), so the workspace size is known
