@@ -197,6 +197,9 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
 
     // q and dO of row i as B operands (lane half hi holds 8 of each 16
     // columns), lse in log2 units, and D = dO . O over the whole row.
+    // Every load is unconditional (a row past N reads row 0, then counts as
+    // zero), so that all of them go out together and one wait covers them:
+    // loads under a branch were issued in pieces with full waits between.
     bf16x8 qf[NQ], df[NV];
     float lse2 = 0.f, dsum = 0.f;
     {
@@ -204,25 +207,24 @@ __global__ __launch_bounds__(kThreads, kDqOccupancy<DQK>) void ssa_bwd_dq_bf16(c
         const uint16_t *qrow = (const uint16_t *)a.q + bb * a.qs[0] + ii * a.qs[1] + h * a.qs[2] + 8 * hi;
         const uint16_t *drow = (const uint16_t *)a.dout + bb * a.dos[0] + ii * a.dos[1] + h * a.dos[2] + 8 * hi;
         const uint16_t *orow = (const uint16_t *)a.o + bb * a.os[0] + ii * a.os[1] + h * a.os[2] + 8 * hi;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks) {
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (row_ok) w = *(const u32x4 *)(qrow + ks * 16);
-            qf[ks] = __builtin_bit_cast(bf16x8, w);
+            const u32x4 w = *(const u32x4 *)(qrow + ks * 16);
+            qf[ks] = __builtin_bit_cast(bf16x8, row_ok ? w : zero);
         }
 #pragma unroll
         for (int ks = 0; ks < NV; ++ks) {
-            u32x4 dw = {0u, 0u, 0u, 0u}, ow = {0u, 0u, 0u, 0u};
-            if (row_ok) {
-                dw = *(const u32x4 *)(drow + ks * 16);
-                ow = *(const u32x4 *)(orow + ks * 16);
-            }
+            u32x4 dw = *(const u32x4 *)(drow + ks * 16), ow = *(const u32x4 *)(orow + ks * 16);
+            dw = row_ok ? dw : zero;
+            ow = row_ok ? ow : zero;
             df[ks] = __builtin_bit_cast(bf16x8, dw);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 dsum += bf16_lo(dw[e]) * bf16_lo(ow[e]) + bf16_hi(dw[e]) * bf16_hi(ow[e]);
         }
-        if (row_ok) lse2 = a.lse[((int64_t)bb * a.Hq + h) * a.N + i] * kLog2e;
+        const float lraw = a.lse[((int64_t)bb * a.Hq + h) * a.N + ii];
+        lse2 = row_ok ? lraw * kLog2e : 0.f;
         if constexpr (kParkDq<DQK>) {
             // Read-only MFMA operands live in AGPRs for the whole tile; the
             // VGPRs hold the accumulators, whose scores feed VALU work.
@@ -518,22 +520,23 @@ __global__ __launch_bounds__(kThreads, 1) void ssa_bwd_dkv_bf16(const BackwardAr
     const bool key_ok = j < a.N;
     const int re_j = key_row_end(a, key_ok ? j : a.N - 1);
     const int up_j = re_j < r1 ? re_j : r1;
+    // Unconditional loads (a key past N reads key 0, then counts as zero),
+    // all issued before one wait.
     bf16x8 kf[NQ], vf[NV];
     {
         const int64_t jj = key_ok ? j : 0;
         const uint16_t *krow = (const uint16_t *)a.k + bb * a.ks[0] + jj * a.ks[1] + g * a.ks[2] + 8 * hi;
         const uint16_t *vrow = (const uint16_t *)a.v + bb * a.vs[0] + jj * a.vs[1] + g * a.vs[2] + 8 * hi;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks) {
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (key_ok) w = *(const u32x4 *)(krow + ks * 16);
-            kf[ks] = __builtin_bit_cast(bf16x8, w);
+            const u32x4 w = *(const u32x4 *)(krow + ks * 16);
+            kf[ks] = __builtin_bit_cast(bf16x8, key_ok ? w : zero);
         }
 #pragma unroll
         for (int ks = 0; ks < NV; ++ks) {
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (key_ok) w = *(const u32x4 *)(vrow + ks * 16);
-            vf[ks] = __builtin_bit_cast(bf16x8, w);
+            const u32x4 w = *(const u32x4 *)(vrow + ks * 16);
+            vf[ks] = __builtin_bit_cast(bf16x8, key_ok ? w : zero);
         }
         // Read-only MFMA operands live in AGPRs for the whole work-group.
 #pragma unroll
