@@ -671,6 +671,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             // and the rounded SSA result this lane stored earlier (a wave's
             // accesses to one address stay in order; the opaque offset keeps
             // the compiler from carrying the stored values in registers).
+            // o_mix overlaps no other buffer, so every piece of the SSA row is
+            // loaded before the first store: one wait, not one per piece.
             const float l_tot = l_run + __shfl_xor(l_run, 32);
             const float wf = a.alpha / l_tot, ws = 1.f - a.alpha;
             int64_t off = bb * a.os[0] + (int64_t)i * a.os[1] + h * a.os[2];
@@ -679,15 +681,19 @@ __global__ __launch_bounds__(kThreads, 2) void ssa_prefill_bf16(const PrefillArg
             const uint16_t *srow = (const uint16_t *)a.o + off;
             auto up = [](uint32_t w, int half) { return __uint_as_float(half ? w & 0xffff0000u : w << 16); };
             if (row_ok) {
+                u32x2 sv[NDB][4];
+#pragma unroll
+                for (int d = 0; d < NDB; ++d)
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) sv[d][rq] = *(const u32x2 *)(srow + d * 32 + 8 * rq + 4 * hi);
 #pragma unroll
                 for (int d = 0; d < NDB; ++d)
 #pragma unroll
                     for (int rq = 0; rq < 4; ++rq) {
-                        const u32x2 sv = *(const u32x2 *)(srow + d * 32 + 8 * rq + 4 * hi);
                         float m[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            m[e] = __builtin_fmaf(oacc[d][4 * rq + e], wf, ws * up(sv[e >> 1], e & 1));
+                            m[e] = __builtin_fmaf(oacc[d][4 * rq + e], wf, ws * up(sv[d][rq][e >> 1], e & 1));
                         *(u32x2 *)(mrow + d * 32 + 8 * rq + 4 * hi) =
                             u32x2{pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3])};
                     }
