@@ -26,9 +26,10 @@
 //    split is a 64x576x(tokens) and a 64x(tokens)x512 product, so it runs on
 //    v_mfma_f32_16x16x32_bf16: S^T = K q^T (one 16-head column block per wave),
 //    then O^T = V^T P^T with P taken straight from the score registers. Chunks
-//    of 32 latent rows stream global -> LDS through a 4-deep ring (a whole
-//    128-token split is requested at once); each row is stored once and the
-//    V^T operand is gathered from it with transpose reads.
+//    of 32 latent rows stream global -> LDS through a 4-deep ring (three
+//    chunks requested at the start, the next one as each chunk is taken);
+//    each row is stored once and the V^T operand is gathered from it with
+//    transpose reads.
 #include <type_traits>
 
 #include "common.h"
@@ -360,7 +361,10 @@ __device__ __forceinline__ int lat_swz(int r) {
 // One work-group computes one split (up to split_tokens attended tokens of
 // one sequence) for up to 64 query heads of one kv head; wave w owns heads
 // 16w..16w+15. The split's latent rows arrive in 32-token chunks through a
-// ring of four LDS buffers (an SSA split of 128 tokens is requested at once).
+// ring of four LDS buffers: three are requested at the start and each chunk,
+// once taken, frees the buffer of the one before it for the chunk three
+// ahead (requesting all four of a 128-token split at the start measured
+// slower: the first chunk then shares the memory system with the fourth).
 // Per chunk: S^T = K q^T, an online softmax with lazy rescaling, and
 // O^T += V^T P^T with P taken straight from the score registers; both
 // products run on v_mfma_f32_16x16x32_bf16 and the V^T operand is gathered
