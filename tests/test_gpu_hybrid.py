@@ -122,6 +122,19 @@ def test_full_size_workload_sampled():
     _case(lens, inputs.HYBRID_K, 64, inputs.HYBRID_PATTERN, seed=inputs.HYBRID_SEED, rows=[0, 7, 19, 31])
 
 
+def test_widest_list_splits():
+    """128 sequences: the planner widens the splits to 1,024 tokens, the most
+    the latent kernel's LDS table of listed rows holds; 1,000 listed tokens
+    per row leave a padded tail in that table. Eight sampled rows against the
+    oracle (the short contexts among them too)."""
+    rng = np.random.default_rng(971)
+    lens = tuple(int(x) for x in rng.integers(1500, 9000, size=128))
+    lens = lens[:5] + (1, 17, 1040) + lens[8:]
+    assert ssa.hybrid_decode_workspace_size(torch.bfloat16, 128, 64, 1, LAT_DQK, LAT_DV, inputs.PAGE_SIZE,
+                                            max(-(-L // inputs.PAGE_SIZE) for L in lens), 1000) > 0
+    _case(lens, 1000, 64, inputs.HYBRID_PATTERN, seed=972, rows=[0, 5, 6, 7, 63, 64, 100, 127])
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("Hq,Hkv,d", [(4, 4, 128), (8, 2, 64), (8, 2, 256), (16, 2, 128)])
 def test_mha_gqa_shapes(dtype, Hq, Hkv, d):
