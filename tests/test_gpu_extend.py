@@ -99,6 +99,17 @@ def test_multi_token_decode_patterns(pattern):
          128 ** -0.5, f"mtp {pattern}")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_multi_token_decode_single_split_windows(dtype):
+    """Windows of at most 128 tokens fit one split, so the decode kernels over
+    query rows write each packed row's output themselves, without a merge
+    (fp32 and d = 256 take the decode kernels at any chunk length)."""
+    d = 128 if dtype == torch.float32 else 256
+    for pattern in (dict(block=32, sink=1, local=3), dict(block=128, sink=0, local=1)):
+        _run(_inp((1, 60, 129, 700, 3000), (1, 7, 8, 3, 6), 4, 2, d, d, dtype=dtype, seed=735), pattern,
+             d ** -0.5, f"mtp single split {dtype} {pattern}")
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
 def test_one_row_chunks_equal_decode_bitwise(Hq, Hkv):
     """bf16 one-row chunks take the decode kernels over query rows: each row
